@@ -1,0 +1,147 @@
+"""fp64 CPU oracle for rotary causal self-attention -- TEST INFRASTRUCTURE.
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The product library never loads it, and it shares no code with
+the GPU path.  The arithmetic lives in oracle.c (plain C, fp64, OpenMP); this
+module only marshals numpy arrays through ctypes.
+
+All tensors are numpy float64 arrays of logical shape [N, H, d]; cu_seqlens is
+an int32 array of S + 1 sequence boundaries.  LSE has shape [H', N'], where
+H' = H/2 and N' = 2N when paired, else H and N.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I32 = ctypes.POINTER(ctypes.c_int32)
+_I64 = ctypes.POINTER(ctypes.c_int64)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = _build.LIB
+    if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+        _build.build()
+    lib = ctypes.CDLL(path)
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_slot_map.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    _I64, ctypes.POINTER(ctypes.c_int)]
+    lib.oracle_rope.argtypes = [_D, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _I32, ctypes.c_int,
+                                ctypes.c_int, ctypes.c_double, ctypes.c_int, _D]
+    common = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, _I32, ctypes.c_int, ctypes.c_int,
+              ctypes.c_int, ctypes.c_int, ctypes.c_double]
+    lib.oracle_attn_fwd.argtypes = [_D, _D, _D] + common + [_D, _D]
+    lib.oracle_attn_fwd_rows.argtypes = [_D, _D, _D] + common + [ctypes.c_int64, _I64, _D, _D]
+    lib.oracle_attn_bwd.argtypes = [_D, _D, _D, _D] + common + [_D, _D, _D]
+    lib.oracle_attn_bwd_sampled.argtypes = ([_D, _D, _D, _D] + common +
+                                            [ctypes.c_int64, _I64, _D, ctypes.c_int64, _I64, _D, _D])
+    for f in (lib.oracle_rope, lib.oracle_attn_fwd, lib.oracle_attn_fwd_rows,
+              lib.oracle_attn_bwd, lib.oracle_attn_bwd_sampled):
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _f64(x):
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _p(a, t=_D):
+    return a.ctypes.data_as(t)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"{name} failed with status {rc}")
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def slot_map(n: int, h: int, H: int, paired: int):
+    """(slot, attention head) of logical token n, head h."""
+    s = ctypes.c_int64()
+    j = ctypes.c_int()
+    _check(_load().oracle_slot_map(n, h, H, paired, ctypes.byref(s), ctypes.byref(j)), "slot_map")
+    return s.value, j.value
+
+
+def rope(x, cu, convention: int, base: float = 10000.0, paired: int = 0):
+    """RoPE of x [N, H, d]; convention 1 = half-split, 2 = adjacent pairs."""
+    x = _f64(x)
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    N, H, d = x.shape
+    y = np.empty_like(x)
+    _check(_load().oracle_rope(_p(x), N, H, d, _p(cu, _I32), len(cu) - 1, convention, base,
+                               paired, _p(y)), "oracle_rope")
+    return y
+
+
+def _heads(H, N, paired):
+    return (H // 2, 2 * N) if paired else (H, N)
+
+
+def attn_fwd(q, k, v, cu, paired=0, causal=1, window=0, scale=0.0):
+    """O [N, H, d] and LSE [H', N'] of softmax(scale q k^T + mask) v."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    N, H, d = q.shape
+    Hs, Ns = _heads(H, N, paired)
+    o = np.empty_like(q)
+    lse = np.empty((Hs, Ns), dtype=np.float64)
+    _check(_load().oracle_attn_fwd(_p(q), _p(k), _p(v), N, H, d, _p(cu, _I32), len(cu) - 1, paired,
+                                   causal, window, scale, _p(o), _p(lse)), "oracle_attn_fwd")
+    return o, lse
+
+
+def attn_fwd_rows(q, k, v, cu, rows, paired=0, causal=1, window=0, scale=0.0):
+    """Forward at selected (attention head, slot) rows: O rows [R, d], LSE [R]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 2)
+    N, H, d = q.shape
+    o = np.empty((len(rows), d), dtype=np.float64)
+    lse = np.empty(len(rows), dtype=np.float64)
+    _check(_load().oracle_attn_fwd_rows(_p(q), _p(k), _p(v), N, H, d, _p(cu, _I32), len(cu) - 1,
+                                        paired, causal, window, scale, len(rows), _p(rows, _I64),
+                                        _p(o), _p(lse)), "oracle_attn_fwd_rows")
+    return o, lse
+
+
+def attn_bwd(q, k, v, dout, cu, paired=0, causal=1, window=0, scale=0.0):
+    """dQ, dK, dV [N, H, d] of L = sum(O * dout)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    N, H, d = q.shape
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    _check(_load().oracle_attn_bwd(_p(q), _p(k), _p(v), _p(dout), N, H, d, _p(cu, _I32),
+                                   len(cu) - 1, paired, causal, window, scale, _p(dq), _p(dk),
+                                   _p(dv)), "oracle_attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_sampled(q, k, v, dout, cu, q_rows, k_cols, paired=0, causal=1, window=0, scale=0.0):
+    """dQ at (head, slot) rows [R, d]; dK, dV at (head, slot) key columns [C, d]."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    q_rows = np.ascontiguousarray(q_rows, dtype=np.int64).reshape(-1, 2)
+    k_cols = np.ascontiguousarray(k_cols, dtype=np.int64).reshape(-1, 2)
+    N, H, d = q.shape
+    dq = np.empty((len(q_rows), d), dtype=np.float64)
+    dk = np.empty((len(k_cols), d), dtype=np.float64)
+    dv = np.empty((len(k_cols), d), dtype=np.float64)
+    _check(_load().oracle_attn_bwd_sampled(_p(q), _p(k), _p(v), _p(dout), N, H, d, _p(cu, _I32),
+                                           len(cu) - 1, paired, causal, window, scale,
+                                           len(q_rows), _p(q_rows, _I64), _p(dq), len(k_cols),
+                                           _p(k_cols, _I64), _p(dk), _p(dv)),
+           "oracle_attn_bwd_sampled")
+    return dq, dk, dv
