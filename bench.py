@@ -1,0 +1,243 @@
+"""Benchmark of the rotary causal self-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: rope_qkv (Q, K rotated), attn_fwd (O, LSE) and, for
+the long-context problem, attn_bwd (dQ, dK, dV).  The plan (work lists and
+rotary table) is built once per batch layout, before the timed region.
+
+Printed: ONE JSON line.  `value` is causal TFLOP/s over the step: the exact
+visible-pair FLOPs of the forward (4 d per pair) plus the backward (2.5x the
+forward), divided by the wall time of the step.  Per-kernel figures come from
+HIP events recorded on the launch stream around every launch of the timed
+steps.  `roofline` is for the kernel that takes the most time; every
+kernel's own roofline is under `kernels`.  `cpu_baseline` times the fp64
+oracle on a bounded sample of the same workload on the host cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 matrix / vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+METRIC = "attention fwd TFLOP/s (causal FLOPs) + % bf16 MFMA peak; rope_qkv HBM GB/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_sources_digest():
+    """Digest of the HIP sources, to tie stored counter readings to a kernel version."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "transformer_causal_self_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel, workload, digest):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    r = rec.get(f"{kernel}@{workload}")
+    if not r or r.get("sources") != digest:
+        return None
+    return r.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, seconds):
+    """fp64 oracle on a bounded random sample of the forward's query rows (plus
+    its RoPE of every token), scaled to causal TFLOP/s."""
+    import numpy as np
+    import oracle
+
+    mult = 2 if w.paired else 1
+    Hs, Ns = w.heads // mult, w.n_tokens * mult
+    cu = inp["cu"]
+    bounds = np.asarray(cu, np.int64) * mult
+
+    def visible(s):
+        k = np.searchsorted(bounds, s, side="right") - 1
+        n = s - bounds[k] + 1
+        return min(n, w.window) if w.window > 0 else n
+
+    rng = np.random.default_rng(0)
+    q = inp["q"].double().numpy()
+    k = inp["k"].double().numpy()
+    v = inp["v"].double().numpy()
+
+    def run(nrows):
+        rows = np.stack([rng.integers(0, Hs, nrows), rng.integers(0, Ns, nrows)], 1)
+        t0 = time.perf_counter()
+        qr = oracle.rope(q, cu, w.rope, w.rope_base, w.paired)
+        kr = oracle.rope(k, cu, w.rope, w.rope_base, w.paired)
+        oracle.attn_fwd_rows(qr, kr, v, cu, rows, w.paired, w.causal, w.window, w.scale)
+        dt = time.perf_counter() - t0
+        flops = sum(4.0 * w.head_dim * visible(int(s)) for s in rows[:, 1])
+        return dt, flops, nrows
+
+    dt, fl, n = run(64)
+    n = int(min(Ns * Hs, max(64, 64 * seconds / max(dt, 1e-3))))
+    dt, fl, n = run(n)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} random (head, query) rows of the forward of this workload plus the "
+                      f"RoPE of every token, fp64, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path is single-GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import transformer_causal_self_amd as tca
+    from transformer_causal_self_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = wl.generate(w)
+    plan = tca.attn_plan_create(w.n_tokens, w.heads, w.head_dim,
+                                "fp32" if w.dtype == wl.DTYPE_FP32 else "bf16", inp["cu"],
+                                causal=w.causal, window=w.window, softmax_scale=w.scale,
+                                rope=w.rope, rope_base=w.rope_base, paired=w.paired).bind(dev)
+    info = plan.info
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    do = inp["do"].to(dev) if w.backward else None
+    q2, k2 = torch.empty_like(q), torch.empty_like(k)
+    o = torch.empty_like(q)
+    lse = torch.empty((info["attn_heads"], info["slots"]), dtype=torch.float32, device=dev)
+    grads = None
+    tca.rope_qkv(plan, q, k, q_out=q2, k_out=k2)
+    tca.attn_fwd(plan, q2, k2, v, o, lse)
+    if w.backward:
+        grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+        try:
+            tca.attn_bwd(plan, q2, k2, v, o, lse, do, *grads)
+        except tca.AttnError as e:
+            if e.status != -2:
+                raise
+            grads = None        # backward kernels not built into this library
+
+    names = ["rope_qkv", "attn_fwd"] + (["attn_bwd"] if grads is not None else [])
+    events = {n: [] for n in names}
+
+    def step(record):
+        def timed(name, fn):
+            if record:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                events[name].append((a, b))
+            else:
+                fn()
+        timed("rope_qkv", lambda: tca.rope_qkv(plan, q, k, q_out=q2, k_out=k2))
+        timed("attn_fwd", lambda: tca.attn_fwd(plan, q2, k2, v, o, lse))
+        if grads is not None:
+            timed("attn_bwd", lambda: tca.attn_bwd(plan, q2, k2, v, o, lse, do, *grads))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    kern_ms = {n: sum(a.elapsed_time(b) for a, b in events[n]) / len(events[n]) for n in names}
+    digest = kernel_sources_digest()
+    wname = f"problem{w.num}"
+    step_flops = info["fwd_flops"] + (info["bwd_flops"] if grads is not None else 0.0)
+    kernels = {}
+    peak_mm = PEAK_BF16_TFLOPS if w.dtype == wl.DTYPE_BF16 else PEAK_FP32_TFLOPS
+    for n in names:
+        t = kern_ms[n] * 1e-3
+        if n == "rope_qkv":
+            ach = info["rope_bytes"] / t / 1e9
+            rl = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                  "frac": ach / PEAK_HBM_GBS}
+        else:
+            fl = info["fwd_flops"] if n == "attn_fwd" else info["bwd_flops"]
+            ach = fl / t / 1e12
+            rl = {"bound": "mfma", "achieved": ach, "peak": peak_mm, "unit": "TFLOP/s",
+                  "frac": ach / peak_mm}
+        rl["traffic"] = stored_traffic(n, wname, digest)
+        rl["ms"] = kern_ms[n]
+        kernels[n] = rl
+    dominant = max(names, key=lambda n: kern_ms[n])
+    roof = {k2_: v_ for k2_, v_ in kernels[dominant].items() if k2_ != "ms"}
+    roof["kernel"] = dominant
+
+    out = {
+        "metric": METRIC,
+        "value": step_flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == wl.DTYPE_BF16 else "fp32",
+        "data": "synthetic (seeded N(0,1) Q, K, V, dO; fixed sequence layout)",
+        "config": {"workload": w.name, "tokens": w.n_tokens, "heads": w.heads,
+                   "head_dim": w.head_dim, "sequences": len(inp["cu"]) - 1,
+                   "window": w.window, "paired": w.paired,
+                   "rope": {1: "half-split", 2: "adjacent"}.get(w.rope, "none"),
+                   "step": "+".join(names), "parallelism": "single GPU"},
+        "roofline": roof,
+        "kernels": kernels,
+        "fwd_tflops": kernels["attn_fwd"]["achieved"],
+        "fwd_frac_bf16_peak": kernels["attn_fwd"]["frac"],
+        "rope_gbs": kernels["rope_qkv"]["achieved"],
+        "step_flops": step_flops,
+        "visible_pairs": info["visible_pairs"],
+        "kernel_sources": digest,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * attn_mi355.h -- C ABI of the MI355X (gfx950) rotary causal self-attention
+ * library (libattn_mi355.so).
+ *
+ * The library computes, on one GPU,
+ *     O = softmax(s * Q' K'^T + mask) V,    LSE = log of the row sums,
+ * with Q', K' the rotary-embedded queries and keys, over packed variable-length
+ * sequences, optionally with a causal sliding window, and optionally with
+ * "paired heads".  The pages this follows:
+ *
+ *  - "Paired Head Attention" record article (hncyxsy.com):
+ *      section "Source 3: paired forward branch" -- the varlen attention call
+ *        with cu_seqlens, causal=True, softmax_scale and a left window, on one
+ *        packed stream;
+ *      sections "Core idea" and "Source 4: Triton kernel interleave indexing"
+ *        -- head h of token t becomes slot 2t + h / (H/2) of attention head
+ *        h mod (H/2): the sequence doubles and the head count halves;
+ *      section "Sequence length and window" -- sequence boundaries double,
+ *        the window (in key slots) does not;
+ *      sections "Zero-copy RoPE", "Staggered rotary", "Source 2: paired
+ *        rotary table" -- adjacent-pair rotation and the paired position
+ *        2t + (h mod 2).
+ *  - "Upgrading a textbook decoder" (juejin.cn): section 2 "RoPE" -- the
+ *    frequencies base^(-2i/d) and the half-split rotation; section 4 --
+ *    FlashAttention computes the same result as the plain definition.
+ *  - "SingleHeadAttention" note (ranhao.site) -- the lower-triangular causal
+ *    mask; "mHC module" article (lshu.cn), sections 2.1-2.2 -- softmax with
+ *    max subtraction.
+ *
+ * Layouts (row-major, element strides):
+ *   Q, K, V, O         [N, H, d]  token-major, each token's H*d values contiguous.
+ *                      When paired the same memory is read as [2N, H/2, d]:
+ *                      slot 2t + h / (H/2), attention head h mod (H/2).
+ *   LSE                float [H', N'] (attention head, slot); natural log.
+ *   dQ, dK, dV         float [N, H, d] (same slot view as Q when paired).
+ *   N' = 2N, H' = H/2 when paired; else N' = N, H' = H.
+ *
+ * Conventions for every call:
+ *   - Every device pointer must be 16-byte aligned and every token stride a
+ *     multiple of 8 elements (bf16) or 4 elements (fp32); else ATTN_E_ALIGN.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Launch functions only enqueue work; they return ATTN_E_HIP when a launch
+ *     or copy is rejected.  Faults during execution surface at the caller's
+ *     next synchronisation.
+ *   - The caller owns every device buffer, the workspace and the stream.  The
+ *     plan owns only host memory and is immutable after attn_plan_bind, so
+ *     several launches may share it.  Launches that share one bound workspace
+ *     may run concurrently except attn_bwd, which writes a scratch area of it.
+ *   - No call throws, aborts or prints.
+ */
+#ifndef ATTN_MI355_H
+#define ATTN_MI355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct attn_plan attn_plan; /* opaque host object */
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_E_INVALID = -1,     /* a bad argument or an inconsistent problem */
+  ATTN_E_UNSUPPORTED = -2, /* a valid problem the kernels do not cover */
+  ATTN_E_ALIGN = -3,       /* a pointer or stride breaks the alignment rule */
+  ATTN_E_WORKSPACE = -4,   /* plan not bound, or workspace missing/too small */
+  ATTN_E_HIP = -5,         /* the HIP runtime rejected a launch or copy */
+  ATTN_E_NOMEM = -6        /* host allocation failed */
+} attn_status;
+
+enum { ATTN_BF16 = 0, ATTN_FP32 = 1 };
+enum { ATTN_ROPE_NONE = 0, ATTN_ROPE_HALF = 1, ATTN_ROPE_ADJACENT = 2 };
+enum { ATTN_UNPAIRED = 0, ATTN_PAIRED = 1 };
+
+typedef struct {
+  int64_t num_tokens;        /* N >= 0 */
+  int32_t num_heads;         /* H >= 1; even when paired */
+  int32_t head_dim;          /* d: 64 or 128 */
+  int32_t dtype;             /* ATTN_BF16 or ATTN_FP32 (I/O type; fp32 accumulate) */
+  const int32_t *cu_seqlens; /* HOST pointer, num_seqs + 1 entries: 0 = cu[0] <= ... <= cu[S] = N */
+  int32_t num_seqs;          /* S >= 1 */
+  int32_t causal;            /* 0 or 1; must be 1 when window > 0 */
+  int32_t window;            /* <= 0: none; else key slot j is visible from query
+                                slot i only if 0 <= i - j < window (self counts) */
+  float softmax_scale;       /* s; 0 selects 1/sqrt(head_dim) */
+  int32_t rope;              /* ATTN_ROPE_NONE, _HALF (pairs i, i+d/2), _ADJACENT (2i, 2i+1) */
+  double rope_base;          /* frequencies base^(-2i/d); e.g. 10000 */
+  int32_t paired;            /* ATTN_UNPAIRED or ATTN_PAIRED */
+} attn_problem;
+
+/* Counts for throughput and roofline reporting (exact, from the plan). */
+typedef struct {
+  int64_t visible_pairs;     /* (query slot, key slot) pairs inside the mask, all heads */
+  double fwd_flops;          /* 4 * d * visible_pairs (QK^T and PV) */
+  double bwd_flops;          /* 2.5 * fwd_flops (five products) */
+  double rope_bytes;         /* read Q, K and write Q', K' once */
+  double fwd_bytes;          /* read Q, K, V and write O, LSE once */
+  double bwd_bytes;          /* read Q, K, V, O, dO, LSE and write dQ, dK, dV once */
+  int64_t fwd_items;         /* work items (attention head x sequence x query tile) */
+  int64_t bwd_items;         /* key-tile work items of the backward */
+  int64_t slots;             /* N' */
+  int32_t attn_heads;        /* H' */
+  int32_t max_positions;     /* rows of the rotary table */
+} attn_plan_info;
+
+/*
+ * Validate a problem and build its host plan: paired slot boundaries
+ * (2 * cu when paired), the per-token rotary positions, the fp64-computed
+ * cos/sin table rounded to fp32, and the tile work lists (fully masked causal
+ * and window tiles are never listed; longest items first).  Host only: makes
+ * no HIP call.  On success *out owns a plan to free with attn_plan_destroy.
+ * Errors: ATTN_E_INVALID (bad field), ATTN_E_UNSUPPORTED (head_dim not 64 or
+ * 128), ATTN_E_NOMEM.
+ */
+attn_status attn_plan_create(const attn_problem *problem, attn_plan **out);
+
+/* Device workspace the plan needs, in bytes (0 for a NULL plan). */
+size_t attn_plan_workspace_bytes(const attn_plan *plan);
+
+/*
+ * Copy the plan's tables and work lists into d_workspace (device memory of at
+ * least attn_plan_workspace_bytes, 256-byte aligned) on `stream`.  The caller
+ * keeps the workspace alive and unchanged while launches use it.  Rebinding
+ * the same plan to another workspace is allowed.
+ */
+attn_status attn_plan_bind(attn_plan *plan, void *d_workspace, size_t bytes, void *stream);
+
+/* Fill *info with the plan's exact counts.  Host only. */
+attn_status attn_plan_stats(const attn_plan *plan, attn_plan_info *info);
+
+/*
+ * Introspection of the tile work lists (host only), for testing and
+ * scheduling analysis.  which = 0: forward items; which = 1: backward key-tile
+ * items.  Each item is 8 int32: {attention head, r0, r1, s0, s1, 0, 0, 0}.
+ * Forward: query slots [r0, r1) of one sequence and the key slots [s0, s1)
+ * any of them may see.  Backward: key slots [r0, r1) and the query slots
+ * [s0, s1) that may see them.  Copies min(count, capacity) items into out
+ * (out may be NULL when capacity is 0) and stores the total count in *count.
+ */
+attn_status attn_plan_work_items(const attn_plan *plan, int32_t which, int32_t *out,
+                                 int64_t capacity, int64_t *count);
+
+/*
+ * Rotary embedding of Q and K ("Upgrading a textbook decoder", section 2;
+ * "Paired Head Attention", "Zero-copy RoPE" and "Staggered rotary"):
+ * token t of its sequence, head h, is rotated by angle p * base^(-2i/d) on
+ * pair i, p = t (unpaired) or 2t + (h mod 2) (paired):
+ *     (a, b) -> (a cos - b sin, b cos + a sin).
+ * q, k: [N, H, d] with token strides q_tok_stride, k_tok_stride (elements,
+ * >= H*d; e.g. 3*H*d for a packed [N, 3, H, d] QKV).  q_out, k_out: dense
+ * [N, H, d]; q_out == q (in place) is allowed when q_tok_stride == H*d, same
+ * for k.  Written dense, the outputs already are the paired interleaved layout.
+ * v / v_out: when v_out is not NULL, V (token stride v_tok_stride) is copied
+ * dense into v_out in the same pass; when v_out is NULL, v is ignored.
+ * The plan's rope mode must not be ATTN_ROPE_NONE (ATTN_E_INVALID).
+ */
+attn_status rope_qkv(const attn_plan *plan, const void *q, int64_t q_tok_stride, const void *k,
+                     int64_t k_tok_stride, const void *v, int64_t v_tok_stride, void *q_out,
+                     void *k_out, void *v_out, void *stream);
+
+/*
+ * Forward attention over the plan's sequences and mask (flash-style: the
+ * N' x N' score matrix never reaches HBM; "Upgrading a textbook decoder",
+ * section 4).  q, k, v, o: dense [N, H, d] in the plan's dtype (q, k already
+ * rotated); lse: float [H', N'].  Every slot of o and lse is written.
+ */
+attn_status attn_fwd(const attn_plan *plan, const void *q, const void *k, const void *v, void *o,
+                     float *lse, void *stream);
+
+/*
+ * Backward of attn_fwd with respect to its inputs q, k, v (the rotated
+ * values), recomputing P = exp(s q k^T - LSE):
+ *     D_i = dO_i . O_i,  dS = P o (dO V^T - D),
+ *     dV = P^T dO,  dQ = s dS K,  dK = s dS^T Q.
+ * q, k, v, o, d_o: dense [N, H, d] in the plan's dtype; lse: float [H', N']
+ * as written by attn_fwd; dq, dk, dv: float [N, H, d], fully overwritten.
+ * bf16 only (ATTN_E_UNSUPPORTED for fp32).  Uses the workspace's scratch
+ * area, so two attn_bwd calls sharing one workspace must not overlap.
+ */
+attn_status attn_bwd(const attn_plan *plan, const void *q, const void *k, const void *v,
+                     const void *o, const float *lse, const void *d_o, float *dq, float *dk,
+                     float *dv, void *stream);
+
+/* Static description of a status code. */
+const char *attn_status_str(attn_status status);
+
+/* Free a plan (NULL is a no-op).  Device memory is the caller's. */
+void attn_plan_destroy(attn_plan *plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355_H */

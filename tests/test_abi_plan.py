@@ -1,0 +1,168 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared entry point,
+validates problems on the host, and its plan (work lists, exact counts) covers
+every visible (query, key) pair exactly as the dense mask does.  No GPU call
+is made here."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import transformer_causal_self_amd as tca
+from transformer_causal_self_amd import workloads as wl
+import brute
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_mi355.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^(?:attn_status|size_t|const char|void)\s*\**\s*(\w+)\s*\(", text, re.M)
+
+
+def test_header_declares_the_boundary():
+    names = set(declared_functions())
+    assert {"attn_plan_create", "attn_plan_workspace_bytes", "attn_plan_bind", "attn_plan_stats",
+            "attn_plan_work_items", "rope_qkv", "attn_fwd", "attn_bwd", "attn_status_str",
+            "attn_plan_destroy"} <= names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tca.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = tca.load_library()
+    for code in range(-6, 1):
+        assert lib.attn_status_str(code)
+
+
+def plan(**kw):
+    args = dict(num_tokens=16, num_heads=2, head_dim=64, dtype="bf16", cu_seqlens=[0, 16],
+                causal=1, window=0, rope="half", paired=0)
+    args.update(kw)
+    return tca.attn_plan_create(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_heads=3, paired=1), -1),                 # odd heads paired
+    (dict(causal=0, window=4), -1),                    # window needs causal
+    (dict(cu_seqlens=[0, 15]), -1),                    # does not end at N
+    (dict(cu_seqlens=[1, 16]), -1),                    # does not start at 0
+    (dict(cu_seqlens=[0, 10, 8, 16]), -1),             # decreasing
+    (dict(num_tokens=-1, cu_seqlens=[0, -1]), -1),
+    (dict(num_heads=0), -1),
+    (dict(dtype=7), -1),
+    (dict(rope=3), -1),
+    (dict(rope_base=0.0), -1),
+    (dict(softmax_scale=float("nan")), -1),
+    (dict(softmax_scale=-1.0), -1),
+    (dict(paired=2, num_heads=4), -1),
+    (dict(head_dim=32), -2),                           # valid, not covered by the kernels
+    (dict(head_dim=96), -2),
+])
+def test_plan_rejects(kw, status):
+    with pytest.raises(tca.AttnError) as e:
+        plan(**kw)
+    assert e.value.status == status
+
+
+def test_empty_problem_is_valid():
+    p = plan(num_tokens=0, cu_seqlens=[0, 0])
+    assert p.info["visible_pairs"] == 0
+    assert p.info["fwd_items"] == 0
+    assert p.workspace_bytes >= 256
+
+
+def dense_pairs(cu, mult, causal, window):
+    return int(brute.dense_mask(list(cu), mult, causal, window).sum())
+
+
+CASES = [
+    ([0, 300], 2, 0, 1, 0),
+    ([0, 1, 64, 65, 193, 193, 322], 2, 0, 1, 0),      # tile-edge lengths and an empty doc
+    ([0, 200, 450], 4, 1, 1, 0),
+    ([0, 130, 400], 6, 1, 1, 128),
+    ([0, 70, 271], 2, 0, 1, 64),
+    ([0, 50, 300], 2, 0, 1, 1),
+    ([0, 129, 300], 4, 1, 1, 129),
+    ([0, 90, 300], 2, 0, 0, 0),
+]
+
+
+@pytest.mark.parametrize("cu,H,paired,causal,window", CASES)
+def test_counts_and_work_lists_cover_the_mask(cu, H, paired, causal, window):
+    N = cu[-1]
+    p = plan(num_tokens=N, num_heads=H, cu_seqlens=cu, paired=paired, causal=causal,
+             window=window)
+    mult = 2 if paired else 1
+    Hs = H // 2 if paired else H
+    mask = brute.dense_mask(cu, mult, causal, window)
+    assert p.info["visible_pairs"] == Hs * int(mask.sum())
+    assert p.info["fwd_flops"] == 4 * 64 * p.info["visible_pairs"]
+    assert p.info["slots"] == N * mult and p.info["attn_heads"] == Hs
+    fwd = p.work_items(0)
+    bwd = p.work_items(1)
+    # forward: every (head, query) row exactly once; its visible keys inside [k0, k1)
+    bounds = np.array(cu) * mult
+    def seq_of(slot):
+        s = np.searchsorted(bounds, slot, side="right") - 1
+        return bounds[s], bounds[s + 1]
+    seen = np.zeros((Hs, N * mult), dtype=int)
+    for head, q0, q1, k0, k1, *_ in fwd:
+        assert 0 < q1 - q0 <= 128
+        seen[head, q0:q1] += 1
+        rows = mask[q0:q1]
+        cols = np.nonzero(rows.any(axis=0))[0]
+        assert cols.min() >= k0 and cols.max() < k1
+        b, e = seq_of(q0)          # the item stays inside one sequence
+        assert b <= q0 < q1 <= e and b <= k0 < k1 <= e
+    assert (seen == 1).all()
+    # backward: every (head, key) column exactly once; the queries that see it in [s0, s1)
+    seen = np.zeros((Hs, N * mult), dtype=int)
+    for head, r0, r1, s0, s1, *_ in bwd:
+        assert 0 < r1 - r0 <= 128
+        seen[head, r0:r1] += 1
+        cols = mask[:, r0:r1]
+        rows = np.nonzero(cols.any(axis=1))[0]
+        assert rows.min() >= s0 and rows.max() < s1
+        b, e = seq_of(r0)
+        assert b <= r0 < r1 <= e and b <= s0 < s1 <= e
+    assert (seen == 1).all()
+    # longest items first
+    steps = np.ceil((fwd[:, 4] - fwd[:, 3]) / 64)
+    assert (np.diff(steps) <= 0).all()
+
+
+@pytest.mark.parametrize("num,pairs", [(1, 33024), (2, 50380800), (5, 1610711040)])
+def test_exact_visible_pairs_of_fixed_layouts(num, pairs):
+    w = wl.WORKLOADS[num]
+    cu = wl.cu_seqlens(w)
+    p = plan(num_tokens=w.n_tokens, num_heads=w.heads, head_dim=w.head_dim,
+             dtype="fp32" if w.dtype else "bf16", cu_seqlens=cu, paired=w.paired,
+             window=w.window)
+    assert p.info["visible_pairs"] == pairs
+    assert p.info["fwd_flops"] == 4 * w.head_dim * pairs
+
+
+@pytest.mark.parametrize("num", [3, 4])
+def test_varlen_layouts_count_like_the_closed_form(num):
+    w = wl.WORKLOADS[num]
+    cu = wl.cu_seqlens(w)
+    assert cu[0] == 0 and cu[-1] == w.n_tokens and (np.diff(cu) > 0).all()
+    lens = np.diff(cu)
+    lo, hi = w.doc_range
+    assert (lens[:-1] >= lo).all() and (lens <= hi).all()
+    p = plan(num_tokens=w.n_tokens, num_heads=w.heads, head_dim=w.head_dim, cu_seqlens=cu,
+             paired=w.paired, window=w.window, rope="adjacent")
+    mult = 2 if w.paired else 1
+    Hs = w.heads // mult
+    # sum over sequences of the per-row count min(i + 1, W), i = row inside the sequence
+    total = 0
+    for L in lens * mult:
+        i = np.arange(L)
+        total += int(np.minimum(i + 1, w.window).sum())
+    assert p.info["visible_pairs"] == Hs * total

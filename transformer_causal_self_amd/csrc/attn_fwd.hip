@@ -1,0 +1,401 @@
+// attn_fwd.hip -- flash-style causal / windowed / varlen attention forward for
+// gfx950 (MI355X), on MFMA matrix cores.
+//
+// What it computes: O = softmax(s Q K^T + mask) V and LSE = log sum exp per
+// query row, per attention head, with the mask of the plan (same sequence,
+// causal, window of W key slots), exactly the plain definition
+// ("mHC module" article, lshu.cn, section 2.1; "SingleHeadAttention" note,
+// ranhao.site, forward()).  The N' x N' score matrix is never written to HBM:
+// it is produced tile by tile on chip with a running max and sum
+// ("Upgrading a textbook decoder", juejin.cn, section 4, FlashAttention: the
+// tiling changes where the result is computed, not the result).
+//
+// gfx950 mapping (one work item = one block of 4 waves = 128 query slots of
+// one attention head; each wave owns 32 query slots):
+//   * Each wave holds its 32 queries as the B operand of
+//     v_mfma_f32_32x32x16_bf16 for the whole item (registers).
+//   * K tiles of 64 key slots are staged in LDS row-major; V tiles are staged
+//     transposed (V^T, d-major) so both PV operands are k-contiguous.
+//   * S^T = K Q^T: with keys as MFMA rows and queries as columns, every lane of
+//     the accumulator holds one query's scores, so the row max and row sum are
+//     in-lane reductions plus one exchange between the two half-waves.
+//   * P^T goes straight from the accumulator registers to the B operand of
+//     O^T += V^T P^T (no LDS round trip): the V^T tile's key columns are stored
+//     in the order in which the accumulator holds them (bits 2 and 3 of the key
+//     index swapped inside each group of 16).
+//   * exp uses v_exp_f32 (2^x) with log2(e) folded into the scale; masking is
+//     applied only on tiles that cross the causal diagonal, the window edge or
+//     the end of the key range; tiles masked for a whole wave are skipped.
+// The fp32 problem uses the same schedule on v_mfma_f32_32x32x2_f32, whose
+// operands hold one element per lane, so no transposed staging is needed.
+#include <type_traits>
+
+#include "attn_internal.h"
+#include "device_common.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int BK = kFwdBK;  // key slots per step
+constexpr float kMinusBig = -1e30f;  // finite start value of the running max
+
+// Key position of key k (0..63 in a tile) inside the transposed V tile.
+__device__ __forceinline__ int vt_pos(int k) {
+  return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+template <typename T, int D>
+struct Smem;
+template <int D>
+struct Smem<__bf16, D> {
+  static constexpr int KS = D + 8;   // K row stride (elements), 16-byte rows, 4-bank shift
+  static constexpr int VS = BK + 8;  // V^T row stride (elements)
+  __bf16 k[BK * KS];
+  __bf16 vt[D * VS];
+};
+template <int D>
+struct Smem<float, D> {
+  static constexpr int KS = D + 1;   // odd stride: column reads hit 32 different banks
+  static constexpr int VS = D + 4;
+  float k[BK * KS];
+  float v[BK * VS];
+};
+
+// Global -> register staging of one K/V tile.
+template <typename T, int D>
+struct Stage;
+
+template <int D>
+struct Stage<__bf16, D> {
+  static constexpr int KPT = BK * D / 8 / kFwdThreads;          // 16B K chunks per thread
+  static constexpr int VPT = (BK / 2) * (D / 8) / kFwdThreads;  // key pairs x 8 d per thread
+  uint4 kr[KPT];
+  uint4 vr[VPT][2];
+
+  __device__ __forceinline__ void load(const __bf16 *Kh, const __bf16 *Vh, int64_t rs, int kt0,
+                                       int k1, int tid) {
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const int ci = tid + kFwdThreads * r;
+      const int key = ci / (D / 8), c8 = ci % (D / 8);
+      const int slot = kt0 + key;
+      kr[r] = slot < k1 ? *reinterpret_cast<const uint4 *>(Kh + slot * rs + 8 * c8)
+                        : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < VPT; ++r) {
+      const int vi = tid + kFwdThreads * r;
+      const int kp = vi % (BK / 2), c8 = vi / (BK / 2);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int slot = kt0 + 2 * kp + e;
+        vr[r][e] = slot < k1 ? *reinterpret_cast<const uint4 *>(Vh + slot * rs + 8 * c8)
+                             : make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(Smem<__bf16, D> &sm, int tid) {
+    constexpr int KS = Smem<__bf16, D>::KS, VS = Smem<__bf16, D>::VS;
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const int ci = tid + kFwdThreads * r;
+      const int key = ci / (D / 8), c8 = ci % (D / 8);
+      *reinterpret_cast<uint4 *>(&sm.k[key * KS + 8 * c8]) = kr[r];
+    }
+#pragma unroll
+    for (int r = 0; r < VPT; ++r) {
+      const int vi = tid + kFwdThreads * r;
+      const int kp = vi % (BK / 2), c8 = vi / (BK / 2);
+      const int pos = vt_pos(2 * kp);  // even; key 2kp+1 lands at pos + 1
+      const uint32_t a[4] = {vr[r][0].x, vr[r][0].y, vr[r][0].z, vr[r][0].w};
+      const uint32_t b[4] = {vr[r][1].x, vr[r][1].y, vr[r][1].z, vr[r][1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t word = (e & 1) ? __byte_perm(a[e / 2], b[e / 2], 0x7632)
+                                      : __byte_perm(a[e / 2], b[e / 2], 0x5410);
+        *reinterpret_cast<uint32_t *>(&sm.vt[(8 * c8 + e) * VS + pos]) = word;
+      }
+    }
+  }
+};
+
+template <int D>
+struct Stage<float, D> {
+  static constexpr int PT = BK * D / 4 / kFwdThreads;  // float4 chunks per thread (K and V)
+  float4 kr[PT];
+  float4 vr[PT];
+
+  __device__ __forceinline__ void load(const float *Kh, const float *Vh, int64_t rs, int kt0,
+                                       int k1, int tid) {
+#pragma unroll
+    for (int r = 0; r < PT; ++r) {
+      const int ci = tid + kFwdThreads * r;
+      const int key = ci / (D / 4), c4 = ci % (D / 4);
+      const int slot = kt0 + key;
+      const bool ok = slot < k1;
+      kr[r] = ok ? *reinterpret_cast<const float4 *>(Kh + slot * rs + 4 * c4)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+      vr[r] = ok ? *reinterpret_cast<const float4 *>(Vh + slot * rs + 4 * c4)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+
+  __device__ __forceinline__ void store(Smem<float, D> &sm, int tid) {
+    constexpr int KS = Smem<float, D>::KS, VS = Smem<float, D>::VS;
+#pragma unroll
+    for (int r = 0; r < PT; ++r) {
+      const int ci = tid + kFwdThreads * r;
+      const int key = ci / (D / 4), c4 = ci % (D / 4);
+      float *kd = &sm.k[key * KS + 4 * c4];
+      kd[0] = kr[r].x;
+      kd[1] = kr[r].y;
+      kd[2] = kr[r].z;
+      kd[3] = kr[r].w;
+      *reinterpret_cast<float4 *>(&sm.v[key * VS + 4 * c4]) = vr[r];
+    }
+  }
+};
+
+// The wave's 32 queries as the MFMA B operand (k = feature index).
+template <typename T, int D>
+struct QFrag;
+template <int D>
+struct QFrag<__bf16, D> {
+  bf16x8 f[D / 16];
+  __device__ __forceinline__ void load(const __bf16 *Qh, int64_t rs, int qi, bool ok, int h) {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      if (ok) {
+        f[c] = *reinterpret_cast<const bf16x8 *>(Qh + qi * rs + 16 * c + 8 * h);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[c][e] = (__bf16)0.0f;
+      }
+    }
+  }
+  // S^T (32 keys x 32 queries) for keys 32*beta .. +32 of the staged tile.
+  __device__ __forceinline__ floatx16 scores(const Smem<__bf16, D> &sm, int beta, int l32,
+                                             int h) const {
+    constexpr int KS = Smem<__bf16, D>::KS;
+    floatx16 acc = {};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const bf16x8 a =
+          *reinterpret_cast<const bf16x8 *>(&sm.k[(32 * beta + l32) * KS + 16 * c + 8 * h]);
+      acc = mfma32x32x16(a, f[c], acc);
+    }
+    return acc;
+  }
+};
+template <int D>
+struct QFrag<float, D> {
+  float f[D / 2];
+  __device__ __forceinline__ void load(const float *Qh, int64_t rs, int qi, bool ok, int h) {
+#pragma unroll
+    for (int c = 0; c < D / 2; ++c) f[c] = ok ? Qh[qi * rs + 2 * c + h] : 0.0f;
+  }
+  __device__ __forceinline__ floatx16 scores(const Smem<float, D> &sm, int beta, int l32,
+                                             int h) const {
+    constexpr int KS = Smem<float, D>::KS;
+    floatx16 acc = {};
+#pragma unroll
+    for (int c = 0; c < D / 2; ++c)
+      acc = mfma32x32x2f32(sm.k[(32 * beta + l32) * KS + 2 * c + h], f[c], acc);
+    return acc;
+  }
+};
+
+// O^T += V^T P^T for the staged tile; p[beta][r] holds the probabilities of
+// key 32*beta + 8*(r/4) + 4*h + r%4 for this lane's query.
+template <int D>
+__device__ __forceinline__ void accumulate_pv(const Smem<__bf16, D> &sm, const floatx16 (&p)[2],
+                                              floatx16 (&o)[D / 32], int l32, int h) {
+  constexpr int VS = Smem<__bf16, D>::VS;
+  bf16x8 pf[2][2];
+#pragma unroll
+  for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[beta][m][e] = (__bf16)p[beta][8 * m + e];
+#pragma unroll
+  for (int dl = 0; dl < D / 32; ++dl)
+#pragma unroll
+    for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
+            &sm.vt[(32 * dl + l32) * VS + 32 * beta + 16 * m + 8 * h]);
+        o[dl] = mfma32x32x16(a, pf[beta][m], o[dl]);
+      }
+}
+template <int D>
+__device__ __forceinline__ void accumulate_pv(const Smem<float, D> &sm, const floatx16 (&p)[2],
+                                              floatx16 (&o)[D / 32], int l32, int h) {
+  constexpr int VS = Smem<float, D>::VS;
+#pragma unroll
+  for (int dl = 0; dl < D / 32; ++dl)
+#pragma unroll
+    for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * beta + 8 * (r / 4) + 4 * h + (r % 4);
+        o[dl] = mfma32x32x2f32(sm.v[key * VS + 32 * dl + l32], p[beta][r], o[dl]);
+      }
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T *dst, const float *x);
+template <>
+__device__ __forceinline__ void store4<__bf16>(__bf16 *dst, const float *x) {
+  *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
+}
+template <>
+__device__ __forceinline__ void store4<float>(float *dst, const float *x) {
+  *reinterpret_cast<float4 *>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+}
+
+// Two blocks per CU for bf16 (8 waves, <= 256 VGPRs each); the fp32 variant
+// holds its queries as D/2 fp32 registers and runs one block per CU.
+template <typename T>
+constexpr int fwd_min_blocks() {
+  return std::is_same<T, float>::value ? 1 : 2;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kFwdThreads, fwd_min_blocks<T>()) void fwd_kernel(
+    const WorkItem *__restrict__ items, const T *__restrict__ Q, const T *__restrict__ K,
+    const T *__restrict__ V, T *__restrict__ O, float *__restrict__ LSE, int Hs, int64_t Ns,
+    float scale, float scale_log2, int causal, int window) {
+  __shared__ __attribute__((aligned(16))) Smem<T, D> sm;
+  const WorkItem it = items[blockIdx.x];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int64_t rs = (int64_t)Hs * D;  // elements between consecutive slots
+  const T *Qh = Q + (int64_t)it.head * D;
+  const T *Kh = K + (int64_t)it.head * D;
+  const T *Vh = V + (int64_t)it.head * D;
+
+  const int wq0 = it.q0 + 32 * w;             // first query of this wave
+  const int wq1 = min(wq0 + 32, it.q1);        // one past its last valid query
+  const int qi = wq0 + l32;                    // this lane's query
+  const bool qok = qi < it.q1;
+
+  QFrag<T, D> qf;
+  qf.load(Qh, rs, qi, qok, h);
+
+  floatx16 o[D / 32];
+#pragma unroll
+  for (int dl = 0; dl < D / 32; ++dl) o[dl] = floatx16{};
+  float m = kMinusBig;  // running max of raw scores q.k
+  float l = 0.0f;       // this lane's part of the running sum
+
+  const int nk = (it.k1 - it.k0 + BK - 1) / BK;
+  Stage<T, D> st;
+  st.load(Kh, Vh, rs, it.k0, it.k1, tid);
+  for (int t = 0; t < nk; ++t) {
+    const int kt0 = it.k0 + t * BK;
+    __syncthreads();
+    st.store(sm, tid);
+    __syncthreads();
+    if (t + 1 < nk) st.load(Kh, Vh, rs, kt0 + BK, it.k1, tid);
+
+    // wave-uniform tile classification
+    const bool active = wq0 < wq1 && !(causal && kt0 > wq1 - 1) &&
+                        !(window > 0 && wq0 - (kt0 + BK - 1) >= window);
+    if (!active) continue;
+    const bool full = (kt0 + BK <= it.k1) && (!causal || kt0 + BK - 1 <= wq0) &&
+                      (window <= 0 || (wq1 - 1) - kt0 < window);
+
+    floatx16 s[2];
+    s[0] = qf.scores(sm, 0, l32, h);
+    s[1] = qf.scores(sm, 1, l32, h);
+    if (!full) {
+#pragma unroll
+      for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kj = kt0 + 32 * beta + 8 * (r / 4) + 4 * h + (r % 4);
+          const bool vis = kj < it.k1 && (!causal || kj <= qi) && (window <= 0 || qi - kj < window);
+          if (!vis) s[beta][r] = -INFINITY;
+        }
+    }
+    // online softmax: new max, rescale, probabilities
+    float mx = s[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+    mx = halves_max(mx);
+    const float m_new = fmaxf(m, mx);
+    const float alpha = exp2f((m - m_new) * scale_log2);
+    m = m_new;
+    const float mb = m_new * scale_log2;
+    float ls = 0.0f;
+#pragma unroll
+    for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = exp2f(fmaf(s[beta][r], scale_log2, -mb));
+        s[beta][r] = pv;
+        ls += pv;
+      }
+    l = fmaf(l, alpha, ls);
+#pragma unroll
+    for (int dl = 0; dl < D / 32; ++dl)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dl][r] *= alpha;
+    accumulate_pv<D>(sm, s, o, l32, h);
+  }
+
+  // epilogue: O = O^T / l, LSE = s * m + ln l
+  const float lt = halves_sum(l);
+  if (qok) {
+    const float inv = 1.0f / lt;
+    T *orow = O + (int64_t)qi * rs + (int64_t)it.head * D;
+#pragma unroll
+    for (int dl = 0; dl < D / 32; ++dl)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = o[dl][4 * b + i] * inv;
+        store4<T>(orow + 32 * dl + 8 * b + 4 * h, x);
+      }
+    if (h == 0) LSE[(int64_t)it.head * Ns + qi] = m * scale + logf(lt);
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const attn_plan *p, const void *q, const void *k, const void *v, void *o,
+                        float *lse, hipStream_t stream) {
+  const WorkItem *items = reinterpret_cast<const WorkItem *>(p->ws + p->off_fwd);
+  const unsigned n = (unsigned)p->fwd.size();
+  if (n == 0) return hipSuccess;
+  const float scale = p->p.scale;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  hipLaunchKernelGGL((fwd_kernel<T, D>), dim3(n), dim3(kFwdThreads), 0, stream, items,
+                     static_cast<const T *>(q), static_cast<const T *>(k),
+                     static_cast<const T *>(v), static_cast<T *>(o), lse, p->p.Hs, p->p.Ns,
+                     scale, scale_log2, p->p.causal, p->p.window);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+attn_status launch_fwd(const attn_plan *p, const void *q, const void *k, const void *v, void *o,
+                       float *lse, hipStream_t stream) {
+  hipError_t e;
+  const bool bf = p->p.dtype == ATTN_BF16;
+  if (p->p.d == 64)
+    e = bf ? launch_typed<__bf16, 64>(p, q, k, v, o, lse, stream)
+           : launch_typed<float, 64>(p, q, k, v, o, lse, stream);
+  else
+    e = bf ? launch_typed<__bf16, 128>(p, q, k, v, o, lse, stream)
+           : launch_typed<float, 128>(p, q, k, v, o, lse, stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+}  // namespace attn

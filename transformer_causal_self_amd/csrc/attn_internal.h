@@ -1,0 +1,70 @@
+// attn_internal.h -- plan layout and tile sizes shared by the host plan and
+// the gfx950 kernels.  Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "../../include/attn_mi355.h"
+
+namespace attn {
+
+// Tile shapes.  The host plan cuts work items with these, the kernels assume
+// them; both sides include this header.
+//   forward (and the dQ pass of the backward): BQ query slots per work item,
+//   BK key slots per inner step.  Four waves, 32 queries per wave.
+constexpr int kFwdBQ = 128;
+constexpr int kFwdBK = 64;
+constexpr int kFwdThreads = 256;
+//   backward dK/dV pass: BKB key slots per work item, BQB query slots per step.
+constexpr int kBwdBK = 128;
+constexpr int kBwdBQ = 64;
+constexpr int kBwdThreads = 256;
+//   rotary: threads per block.
+constexpr int kRopeThreads = 256;
+
+// One work item of the forward / dQ pass: attention head `head`, query slots
+// [q0, q1) inside one sequence, key slots [k0, k1) that any of those queries
+// may see.  For the dK/dV pass the roles swap: keys [q0, q1) of the item,
+// queries [k0, k1) that may see them.
+struct WorkItem {
+  int32_t head;
+  int32_t q0, q1;
+  int32_t k0, k1;
+  int32_t pad0, pad1, pad2;
+};
+static_assert(sizeof(WorkItem) == 32, "work item is 32 bytes");
+
+struct Problem {
+  int64_t N;       // tokens
+  int32_t H, d;    // heads given, head dim
+  int32_t dtype;   // ATTN_BF16 / ATTN_FP32
+  int32_t causal, window;
+  float scale;
+  int32_t rope;
+  double rope_base;
+  int32_t paired;
+  int32_t Hs;      // attention heads
+  int64_t Ns;      // slots
+};
+
+}  // namespace attn
+
+struct attn_plan {
+  attn::Problem p;
+  std::vector<int32_t> cu;          // token boundaries, S + 1
+  std::vector<int32_t> tok_pos;     // per token: offset inside its sequence
+  std::vector<float> rope_cos;      // [P, d/2]
+  std::vector<float> rope_sin;      // [P, d/2]
+  int32_t max_pos = 0;              // P
+  std::vector<attn::WorkItem> fwd;  // forward / dQ items, longest first
+  std::vector<attn::WorkItem> bwd;  // dK/dV items, longest first
+  attn_plan_info info{};
+
+  // Workspace layout (byte offsets; every section 256-byte aligned).
+  size_t off_pos = 0, off_cos = 0, off_sin = 0, off_fwd = 0, off_bwd = 0, off_delta = 0;
+  size_t ws_bytes = 0;
+  // Bound workspace.
+  char *ws = nullptr;
+};

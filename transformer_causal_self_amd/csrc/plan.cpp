@@ -1,0 +1,301 @@
+// plan.cpp -- host side of the library: problem validation, the plan
+// (rotary table, per-token positions, tile work lists, exact counts), the
+// workspace binding and the C-ABI entry points that check arguments before
+// handing over to the gfx950 launchers.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include <hip/hip_runtime_api.h>
+
+#include "attn_internal.h"
+#include "launch.h"
+
+using attn::WorkItem;
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Visible (query, key) pairs of one sequence of L slots: the lower triangle
+// with the diagonal, cut to a band of `window` diagonals when window > 0
+// ("Paired Head Attention", section "Sequence length and window").
+int64_t visible_pairs_of(int64_t L, int causal, int window) {
+  if (L <= 0) return 0;
+  if (!causal) return L * L;
+  if (window <= 0 || L <= window) return L * (L + 1) / 2;
+  const int64_t W = window;
+  return W * (W + 1) / 2 + (L - W) * W;
+}
+
+// Tiles of `tile` slots of [b, e), each with the span of partner slots that
+// can see it / be seen by it; appended as work items of `head`.
+// forward=true:  item rows are queries, span = visible keys.
+// forward=false: item rows are keys, span = queries that see them.
+void cut_items(std::vector<WorkItem> &out, int head, int64_t b, int64_t e, int tile, int causal,
+               int window, bool forward) {
+  for (int64_t r0 = b; r0 < e; r0 += tile) {
+    const int64_t r1 = std::min<int64_t>(r0 + tile, e);
+    int64_t s0, s1;
+    if (forward) {
+      s0 = (window > 0) ? std::max<int64_t>(b, r0 - window + 1) : b;
+      s1 = causal ? r1 : e;
+    } else {
+      s0 = causal ? r0 : b;
+      s1 = (window > 0) ? std::min<int64_t>(e, r1 - 1 + window) : e;
+    }
+    WorkItem w{};
+    w.head = head;
+    w.q0 = (int32_t)r0;
+    w.q1 = (int32_t)r1;
+    w.k0 = (int32_t)s0;
+    w.k1 = (int32_t)s1;
+    out.push_back(w);
+  }
+}
+
+// Longest first: items with more inner steps start earlier, so the tail of
+// the grid is made of short items (causal load balance).
+void sort_longest_first(std::vector<WorkItem> &v, int step) {
+  std::stable_sort(v.begin(), v.end(), [step](const WorkItem &a, const WorkItem &b) {
+    const int64_t na = (a.k1 - a.k0 + step - 1) / step;
+    const int64_t nb = (b.k1 - b.k0 + step - 1) / step;
+    return na > nb;
+  });
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_status_str(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_E_INVALID: return "invalid argument";
+    case ATTN_E_UNSUPPORTED: return "unsupported problem";
+    case ATTN_E_ALIGN: return "misaligned pointer or stride";
+    case ATTN_E_WORKSPACE: return "plan not bound or workspace too small";
+    case ATTN_E_HIP: return "HIP runtime error";
+    case ATTN_E_NOMEM: return "host allocation failed";
+  }
+  return "unknown status";
+}
+
+attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
+  if (!out) return ATTN_E_INVALID;
+  *out = nullptr;
+  if (!pr || !pr->cu_seqlens) return ATTN_E_INVALID;
+  if (pr->num_tokens < 0 || pr->num_heads < 1 || pr->num_seqs < 1) return ATTN_E_INVALID;
+  if (pr->dtype != ATTN_BF16 && pr->dtype != ATTN_FP32) return ATTN_E_INVALID;
+  if (pr->causal != 0 && pr->causal != 1) return ATTN_E_INVALID;
+  if (pr->window > 0 && !pr->causal) return ATTN_E_INVALID;
+  if (pr->rope < ATTN_ROPE_NONE || pr->rope > ATTN_ROPE_ADJACENT) return ATTN_E_INVALID;
+  if (pr->rope != ATTN_ROPE_NONE && !(pr->rope_base > 0.0 && std::isfinite(pr->rope_base)))
+    return ATTN_E_INVALID;
+  if (pr->paired != ATTN_UNPAIRED && pr->paired != ATTN_PAIRED) return ATTN_E_INVALID;
+  if (pr->paired && (pr->num_heads % 2)) return ATTN_E_INVALID;
+  if (!std::isfinite(pr->softmax_scale) || pr->softmax_scale < 0.0f) return ATTN_E_INVALID;
+  if (pr->head_dim <= 0 || (pr->head_dim % 2)) return ATTN_E_INVALID;
+  const int mult = pr->paired ? 2 : 1;
+  // slots are int32 inside the kernels
+  if (pr->num_tokens * mult > (int64_t(1) << 30)) return ATTN_E_UNSUPPORTED;
+  const int32_t *cu = pr->cu_seqlens;
+  const int S = pr->num_seqs;
+  if (cu[0] != 0 || (int64_t)cu[S] != pr->num_tokens) return ATTN_E_INVALID;
+  int64_t max_len = 0;
+  for (int i = 0; i < S; ++i) {
+    if (cu[i + 1] < cu[i]) return ATTN_E_INVALID;
+    max_len = std::max<int64_t>(max_len, cu[i + 1] - cu[i]);
+  }
+  if (pr->head_dim != 64 && pr->head_dim != 128) return ATTN_E_UNSUPPORTED;
+
+  attn_plan *p = new (std::nothrow) attn_plan();
+  if (!p) return ATTN_E_NOMEM;
+  try {
+    attn::Problem &P = p->p;
+    P.N = pr->num_tokens;
+    P.H = pr->num_heads;
+    P.d = pr->head_dim;
+    P.dtype = pr->dtype;
+    P.causal = pr->causal;
+    P.window = pr->window > 0 ? pr->window : 0;
+    P.scale = pr->softmax_scale == 0.0f ? (float)(1.0 / std::sqrt((double)pr->head_dim))
+                                         : pr->softmax_scale;
+    P.rope = pr->rope;
+    P.rope_base = pr->rope_base;
+    P.paired = pr->paired;
+    P.Hs = pr->paired ? P.H / 2 : P.H;
+    P.Ns = P.N * mult;
+    p->cu.assign(cu, cu + S + 1);
+
+    // Per-token offset inside its sequence (positions restart per sequence).
+    p->tok_pos.resize((size_t)P.N);
+    for (int s = 0; s < S; ++s)
+      for (int32_t n = cu[s]; n < cu[s + 1]; ++n) p->tok_pos[(size_t)n] = n - cu[s];
+
+    // Rotary table: cos and sin of p * base^(-2i/d), computed in fp64 and
+    // rounded once to fp32 ("Upgrading a textbook decoder", section 2).  Paired
+    // positions reach 2t + 1, so the table doubles.
+    if (P.rope != ATTN_ROPE_NONE) {
+      const int half = P.d / 2;
+      p->max_pos = (int32_t)std::max<int64_t>(1, max_len * mult);
+      p->rope_cos.resize((size_t)p->max_pos * half);
+      p->rope_sin.resize((size_t)p->max_pos * half);
+      std::vector<double> theta(half);
+      for (int i = 0; i < half; ++i) theta[i] = std::pow(P.rope_base, -2.0 * i / (double)P.d);
+      for (int32_t pos = 0; pos < p->max_pos; ++pos)
+        for (int i = 0; i < half; ++i) {
+          const double phi = (double)pos * theta[i];
+          p->rope_cos[(size_t)pos * half + i] = (float)std::cos(phi);
+          p->rope_sin[(size_t)pos * half + i] = (float)std::sin(phi);
+        }
+    }
+
+    // Work lists and exact counts.
+    int64_t pairs = 0;
+    for (int j = 0; j < P.Hs; ++j)
+      for (int s = 0; s < S; ++s) {
+        const int64_t b = (int64_t)cu[s] * mult, e = (int64_t)cu[s + 1] * mult;
+        if (e == b) continue;
+        pairs += visible_pairs_of(e - b, P.causal, P.window);
+        cut_items(p->fwd, j, b, e, attn::kFwdBQ, P.causal, P.window, true);
+        cut_items(p->bwd, j, b, e, attn::kBwdBK, P.causal, P.window, false);
+      }
+    sort_longest_first(p->fwd, attn::kFwdBK);
+    sort_longest_first(p->bwd, attn::kBwdBQ);
+
+    const double elems = (double)P.N * P.H * P.d;
+    const double es = P.dtype == ATTN_BF16 ? 2.0 : 4.0;
+    const double lse_bytes = 4.0 * (double)P.Ns * P.Hs;
+    attn_plan_info &I = p->info;
+    I.visible_pairs = pairs;
+    I.fwd_flops = 4.0 * P.d * (double)pairs;
+    I.bwd_flops = 2.5 * I.fwd_flops;
+    I.rope_bytes = 4.0 * elems * es;
+    I.fwd_bytes = 4.0 * elems * es + lse_bytes;
+    I.bwd_bytes = 5.0 * elems * es + lse_bytes + 3.0 * elems * 4.0;
+    I.fwd_items = (int64_t)p->fwd.size();
+    I.bwd_items = (int64_t)p->bwd.size();
+    I.slots = P.Ns;
+    I.attn_heads = P.Hs;
+    I.max_positions = p->max_pos;
+
+    // Workspace layout.
+    size_t off = 0;
+    p->off_pos = off;
+    off = align256(off + sizeof(int32_t) * p->tok_pos.size());
+    p->off_cos = off;
+    off = align256(off + sizeof(float) * p->rope_cos.size());
+    p->off_sin = off;
+    off = align256(off + sizeof(float) * p->rope_sin.size());
+    p->off_fwd = off;
+    off = align256(off + sizeof(WorkItem) * p->fwd.size());
+    p->off_bwd = off;
+    off = align256(off + sizeof(WorkItem) * p->bwd.size());
+    p->off_delta = off;
+    off = align256(off + sizeof(float) * (size_t)P.Ns * P.Hs);
+    p->ws_bytes = std::max<size_t>(off, 256);
+  } catch (const std::bad_alloc &) {
+    delete p;
+    return ATTN_E_NOMEM;
+  }
+  *out = p;
+  return ATTN_OK;
+}
+
+size_t attn_plan_workspace_bytes(const attn_plan *p) { return p ? p->ws_bytes : 0; }
+
+attn_status attn_plan_bind(attn_plan *p, void *ws, size_t bytes, void *stream) {
+  if (!p || !ws) return ATTN_E_INVALID;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return ATTN_E_ALIGN;
+  if (bytes < p->ws_bytes) return ATTN_E_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char *base = static_cast<char *>(ws);
+  struct Sec {
+    size_t off;
+    const void *src;
+    size_t n;
+  } secs[] = {
+      {p->off_pos, p->tok_pos.data(), sizeof(int32_t) * p->tok_pos.size()},
+      {p->off_cos, p->rope_cos.data(), sizeof(float) * p->rope_cos.size()},
+      {p->off_sin, p->rope_sin.data(), sizeof(float) * p->rope_sin.size()},
+      {p->off_fwd, p->fwd.data(), sizeof(WorkItem) * p->fwd.size()},
+      {p->off_bwd, p->bwd.data(), sizeof(WorkItem) * p->bwd.size()},
+  };
+  for (const Sec &s : secs) {
+    if (s.n == 0) continue;
+    if (hipMemcpyAsync(base + s.off, s.src, s.n, hipMemcpyHostToDevice, st) != hipSuccess)
+      return ATTN_E_HIP;
+  }
+  p->ws = base;
+  return ATTN_OK;
+}
+
+attn_status attn_plan_stats(const attn_plan *p, attn_plan_info *info) {
+  if (!p || !info) return ATTN_E_INVALID;
+  *info = p->info;
+  return ATTN_OK;
+}
+
+attn_status attn_plan_work_items(const attn_plan *p, int32_t which, int32_t *out,
+                                 int64_t capacity, int64_t *count) {
+  if (!p || !count || (which != 0 && which != 1) || capacity < 0) return ATTN_E_INVALID;
+  const std::vector<WorkItem> &v = which == 0 ? p->fwd : p->bwd;
+  *count = (int64_t)v.size();
+  const int64_t n = std::min<int64_t>(capacity, (int64_t)v.size());
+  if (n > 0 && !out) return ATTN_E_INVALID;
+  if (n > 0) std::memcpy(out, v.data(), sizeof(WorkItem) * (size_t)n);
+  return ATTN_OK;
+}
+
+void attn_plan_destroy(attn_plan *p) { delete p; }
+
+attn_status rope_qkv(const attn_plan *p, const void *q, int64_t qs, const void *k, int64_t ks,
+                     const void *v, int64_t vs, void *q_out, void *k_out, void *v_out,
+                     void *stream) {
+  if (!p) return ATTN_E_INVALID;
+  if (p->p.rope == ATTN_ROPE_NONE) return ATTN_E_INVALID;
+  if (!p->ws) return ATTN_E_WORKSPACE;
+  const int64_t row = (int64_t)p->p.H * p->p.d;
+  if (p->p.N == 0) return ATTN_OK;
+  if (!q || !k || !q_out || !k_out || (v_out && !v)) return ATTN_E_INVALID;
+  if (qs < row || ks < row || (v_out && vs < row)) return ATTN_E_INVALID;
+  const int64_t vec = p->p.dtype == ATTN_BF16 ? 8 : 4;
+  if (qs % vec || ks % vec || (v_out && vs % vec)) return ATTN_E_ALIGN;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_out) || !aligned16(k_out) ||
+      (v_out && (!aligned16(v) || !aligned16(v_out))))
+    return ATTN_E_ALIGN;
+  if ((q_out == q && qs != row) || (k_out == k && ks != row)) return ATTN_E_INVALID;
+  return attn::launch_rope(p, q, qs, k, ks, v_out ? v : nullptr, vs, q_out, k_out, v_out,
+                           static_cast<hipStream_t>(stream));
+}
+
+attn_status attn_fwd(const attn_plan *p, const void *q, const void *k, const void *v, void *o,
+                     float *lse, void *stream) {
+  if (!p) return ATTN_E_INVALID;
+  if (!p->ws) return ATTN_E_WORKSPACE;
+  if (p->p.N == 0) return ATTN_OK;
+  if (!q || !k || !v || !o || !lse) return ATTN_E_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_E_ALIGN;
+  return attn::launch_fwd(p, q, k, v, o, lse, static_cast<hipStream_t>(stream));
+}
+
+attn_status attn_bwd(const attn_plan *p, const void *q, const void *k, const void *v,
+                     const void *o, const float *lse, const void *d_o, float *dq, float *dk,
+                     float *dv, void *stream) {
+  if (!p) return ATTN_E_INVALID;
+  if (p->p.dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
+  if (!p->ws) return ATTN_E_WORKSPACE;
+  if (p->p.N == 0) return ATTN_OK;
+  if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv) return ATTN_E_INVALID;
+  const void *ptrs[] = {q, k, v, o, lse, d_o, dq, dk, dv};
+  for (const void *x : ptrs)
+    if (!aligned16(x)) return ATTN_E_ALIGN;
+  return attn::launch_bwd(p, q, k, v, o, lse, d_o, dq, dk, dv, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
