@@ -1,0 +1,127 @@
+"""GPU parity of attn_bwd (dQ, dK, dV of the rotated inputs) against the fp64
+oracle's chain-rule backward, through the C ABI.
+
+The GPU forward and backward both run on the oracle's rotated, bf16-rounded
+Q', K' (so the oracle receives nothing from the GPU).  Gradients are stored
+in fp32 but computed on bf16 MFMA, so the bf16 bound (2e-2) applies.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_causal_self_amd as tca
+from transformer_causal_self_amd import workloads as wl
+from parity import assert_close, f64, make_plan, oracle_rotated, say, slot_to_token, tol
+
+pytestmark = pytest.mark.gpu
+
+W = wl.WORKLOADS
+
+
+def gpu_fwd_bwd(w, inp, qt, kt):
+    plan = make_plan(w, inp["cu"])
+    q, k, v, do = qt.cuda(), kt.cuda(), inp["v"].cuda(), inp["do"].cuda()
+    o, lse = tca.attn_fwd(plan, q, k, v)
+    dq, dk, dv = tca.attn_bwd(plan, q, k, v, o, lse, do)
+    torch.cuda.synchronize()
+    return [x.cpu().double().numpy() for x in (dq, dk, dv)]
+
+
+def oracle_bwd(w, inp, qt, kt):
+    return oracle.attn_bwd(f64(qt), f64(kt), f64(inp["v"]), f64(inp["do"]), inp["cu"], w.paired,
+                           w.causal, w.window, w.scale)
+
+
+CASES = [
+    # name, workload
+    ("long-context T=1000", W[5].scaled(1000)),
+    ("long-context T=1500 two sequences", dataclasses.replace(W[5], n_tokens=1500, batch=2)),
+    ("varlen window 2048 d128", W[4].scaled(3000, doc_range=(300, 1400))),
+    ("paired varlen window 128 d128", W[3].scaled(1200, doc_range=(100, 700))),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_bwd_reduced(case):
+    name, w = case
+    w = dataclasses.replace(w, backward=True)
+    inp = wl.generate(w, with_grad=True)
+    say(f"bwd {name}")
+    _, _, qt, kt = oracle_rotated(w, inp)
+    got = gpu_fwd_bwd(w, inp, qt, kt)
+    ref = oracle_bwd(w, inp, qt, kt)
+    for g, r, n in zip(got, ref, ("dQ", "dK", "dV")):
+        assert_close(g, r, tol(w), n)
+
+
+EDGE = [
+    # name, H, d, cu, paired, window, rope
+    ("tile-edge lengths", 2, 64, [0, 1, 64, 127, 191, 319, 448, 577], 0, 0, 1),
+    ("empty sequences d128", 2, 128, [0, 0, 65, 65, 194, 194], 0, 0, 2),
+    ("window 1", 2, 64, [0, 300], 0, 1, 1),
+    ("window 129", 2, 64, [0, 40, 500], 0, 129, 1),
+    ("paired H6 window 129", 6, 64, [0, 97, 301], 1, 129, 2),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_bwd_edge_cases(case):
+    name, H, d, cu, paired, window, rope = case
+    w = dataclasses.replace(W[5], n_tokens=cu[-1], heads=H, head_dim=d, paired=paired,
+                            window=window, rope=rope, doc_range=None, batch=1)
+    inp = wl.tensors(w, seed=21, with_grad=True)
+    inp["cu"] = np.array(cu, np.int32)
+    say(f"bwd edge case {name}")
+    _, _, qt, kt = oracle_rotated(w, inp)
+    got = gpu_fwd_bwd(w, inp, qt, kt)
+    ref = oracle_bwd(w, inp, qt, kt)
+    for g, r, n in zip(got, ref, ("dQ", "dK", "dV")):
+        assert_close(g, r, tol(w), n)
+
+
+def test_bwd_full_size_sampled():
+    """The full long-context problem (T=16384, H=12, d=64); the oracle computes
+    sampled dQ rows and dK/dV columns."""
+    w = W[5]
+    inp = wl.generate(w)
+    say("bwd full long-context problem")
+    _, _, qt, kt = oracle_rotated(w, inp)
+    dq, dk, dv = gpu_fwd_bwd(w, inp, qt, kt)
+    for x in (dq, dk, dv):
+        assert np.isfinite(x).all()
+    rng = np.random.default_rng(5)
+    T, Hs = w.n_tokens, w.heads
+    q_rows = [(int(rng.integers(Hs)), int(s)) for s in
+              list(rng.integers(0, T, 24)) + [0, 1, 127, 128, T - 1]]
+    k_cols = [(int(rng.integers(Hs)), int(s)) for s in
+              list(rng.integers(0, T, 16)) + [0, 1, 63, 64, T - 1]]
+    sq, sk, sv = oracle.attn_bwd_sampled(f64(qt), f64(kt), f64(inp["v"]), f64(inp["do"]),
+                                         inp["cu"], q_rows, k_cols, 0, 1, 0, 0.0)
+    assert_close(np.stack([dq[s, j] for j, s in q_rows]), sq, tol(w), "dQ rows")
+    assert_close(np.stack([dk[s, j] for j, s in k_cols]), sk, tol(w), "dK cols")
+    assert_close(np.stack([dv[s, j] for j, s in k_cols]), sv, tol(w), "dV cols")
+
+
+def test_bwd_deterministic():
+    w = dataclasses.replace(W[4].scaled(3000, doc_range=(300, 1400)), backward=True)
+    inp = wl.generate(w, with_grad=True)
+    _, _, qt, kt = oracle_rotated(w, inp)
+    a = gpu_fwd_bwd(w, inp, qt, kt)
+    b = gpu_fwd_bwd(w, inp, qt, kt)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_bwd_fp32_is_unsupported():
+    w = W[1]
+    inp = wl.generate(w, with_grad=True)
+    plan = make_plan(w, inp["cu"])
+    q = inp["q"].cuda()
+    lse = torch.empty((w.heads, w.n_tokens), device="cuda")
+    with pytest.raises(tca.AttnError) as e:
+        tca.attn_bwd(plan, q, q, q, q, lse, q,
+                     *(torch.empty(q.shape, device="cuda") for _ in range(3)))
+    assert e.value.status == -2

@@ -1,13 +1,403 @@
-// attn_bwd.hip -- attention backward for gfx950 (placeholder until the
-// kernels land: reports the problem as unsupported).
+// attn_bwd.hip -- attention backward for gfx950 (bf16 inputs, fp32 gradients).
+//
+// What it computes: the gradients of L = sum(O * dO) through
+// O = softmax(s Q K^T + mask) V with respect to Q, K, V (the rotated inputs
+// of the forward), from the chain rule with the softmax Jacobian
+// diag(P) - P P^T:
+//     D_i  = dO_i . O_i
+//     P    = exp(s q_i . k_j - LSE_i)           (recomputed from the forward's LSE)
+//     dS   = P o (dO V^T - D)
+//     dV   = P^T dO,   dK = s dS^T Q,   dQ = s dS K.
+// The softmax derivative is the standard one, P o (dP - rowsum(dP o P)) with
+// rowsum(dP o P) = D_i, not the variant printed in the "mHC module" article
+// (lshu.cn, section 4.1), which is not the derivative of softmax.
+//
+// Three kernels, deterministic (no atomics):
+//   1. delta:  D_i for every (attention head, slot).
+//   2. dK/dV:  one block per 128-key tile of one attention head (32 keys per
+//              wave), looping over the 64-query tiles that can see it.  S is
+//              formed as Q K^T so that every accumulator lane belongs to one
+//              key; P^T and dS^T then feed the MFMA A operand straight from
+//              registers, and Q^T / dO^T are staged transposed in LDS with the
+//              matching row permutation.
+//   3. dQ:     one block per 128-query tile (the forward's work list), looping
+//              over key tiles; S^T = K Q^T as in the forward, K^T staged
+//              transposed for dQ^T = K^T dS^T.
 #include "attn_internal.h"
+#include "device_common.h"
 #include "launch.h"
 
 namespace attn {
+namespace {
 
-attn_status launch_bwd(const attn_plan *, const void *, const void *, const void *, const void *,
-                       const float *, const void *, float *, float *, float *, hipStream_t) {
-  return ATTN_E_UNSUPPORTED;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float dot8(const uint4 &a, const uint4 &b) {
+  const uint32_t x[4] = {a.x, a.y, a.z, a.w}, y[4] = {b.x, b.y, b.z, b.w};
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s = fmaf(bf16_lo(x[i]), bf16_lo(y[i]), s);
+    s = fmaf(bf16_hi(x[i]), bf16_hi(y[i]), s);
+  }
+  return s;
+}
+
+// D[head][slot] = dO . O over the head dimension.
+template <int D>
+__global__ __launch_bounds__(256) void delta_kernel(const __bf16 *__restrict__ O,
+                                                    const __bf16 *__restrict__ dO,
+                                                    float *__restrict__ delta, int Hs,
+                                                    int64_t Ns) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;  // slot * Hs + head
+  if (r >= Ns * Hs) return;
+  const uint4 *o4 = reinterpret_cast<const uint4 *>(O + r * D);
+  const uint4 *g4 = reinterpret_cast<const uint4 *>(dO + r * D);
+  float acc = 0.0f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) acc += dot8(o4[c], g4[c]);
+  delta[(r % Hs) * Ns + r / Hs] = acc;
+}
+
+// The two bf16 values at position e (0..7) of two 16-byte rows, as one word
+// (first row in the low half).
+__device__ __forceinline__ uint32_t pair_word(const uint4 &a, const uint4 &b, int e) {
+  const uint32_t x[4] = {a.x, a.y, a.z, a.w}, y[4] = {b.x, b.y, b.z, b.w};
+  return (e & 1) ? __byte_perm(x[e / 2], y[e / 2], 0x7632) : __byte_perm(x[e / 2], y[e / 2], 0x5410);
+}
+
+// Stage rows [t0, t0 + 64) of a [slots, Hs, D] tensor (rows >= lim read as
+// zero): `nat` gets the rows as they are (row stride D + 8), `tr` (optional)
+// the transpose with rows permuted by perm16 (row stride 72).  Work unit of a
+// thread: a pair of rows x 8 features.
+template <int D>
+struct PairStage {
+  static constexpr int UNITS = 32 * (D / 8);
+  static constexpr int PT = UNITS / 256;  // units per thread
+  uint4 r[PT][2];
+  __device__ __forceinline__ void load(const __bf16 *base, int64_t rs, int t0, int lim, int tid) {
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int id = tid + 256 * u;
+      const int rp = id % 32, c8 = id / 32;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int row = t0 + 2 * rp + e;
+        r[u][e] = row < lim ? *reinterpret_cast<const uint4 *>(base + row * rs + 8 * c8)
+                            : make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(__bf16 *nat, __bf16 *tr, int tid) const {
+    constexpr int RS = D + 8, TS = 72;
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int id = tid + 256 * u;
+      const int rp = id % 32, c8 = id / 32;
+      *reinterpret_cast<uint4 *>(&nat[(2 * rp) * RS + 8 * c8]) = r[u][0];
+      *reinterpret_cast<uint4 *>(&nat[(2 * rp + 1) * RS + 8 * c8]) = r[u][1];
+      if (tr) {
+        const int pos = perm16(2 * rp);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<uint32_t *>(&tr[(8 * c8 + e) * TS + pos]) = pair_word(r[u][0], r[u][1], e);
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const floatx16 &x, int first) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[first + e];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const __bf16 *p) {
+  return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+template <int D>
+constexpr int bwd_min_blocks() {
+  return D == 64 ? 2 : 1;
+}
+
+// ---------------------------------------------------------------- dK, dV --
+
+template <int D>
+struct DkvSmem {
+  static constexpr int RS = D + 8, TS = 72, BQ = kBwdBQ;
+  __bf16 q[BQ * RS];
+  __bf16 g[BQ * RS];
+  __bf16 qt[D * TS];
+  __bf16 gt[D * TS];
+  float lse2[BQ];  // LSE * log2(e)
+  float dl[BQ];    // D
+};
+
+template <int D>
+__global__ __launch_bounds__(kBwdThreads, bwd_min_blocks<D>()) void dkv_kernel(
+    const WorkItem *__restrict__ items, const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
+    const __bf16 *__restrict__ V, const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
+    const float *__restrict__ delta, float *__restrict__ dK, float *__restrict__ dV, int Hs,
+    int64_t Ns, float scale, float scale_log2, int causal, int window) {
+  constexpr int RS = DkvSmem<D>::RS, TS = DkvSmem<D>::TS, BQ = kBwdBQ;
+  __shared__ __attribute__((aligned(16))) DkvSmem<D> sm;
+  const WorkItem it = items[blockIdx.x];  // keys [q0, q1), queries [k0, k1)
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int64_t rs = (int64_t)Hs * D;
+  const int64_t ho = (int64_t)it.head * D;
+  const int wk0 = it.q0 + 32 * w, wk1 = min(wk0 + 32, it.q1);
+  const int kj = wk0 + l32;  // this lane's key (column of S)
+  const bool kok = kj < it.q1;
+
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    if (kok) {
+      kf[c] = load_bf16x8(K + ho + kj * rs + 16 * c + 8 * h);
+      vf[c] = load_bf16x8(V + ho + kj * rs + 16 * c + 8 * h);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[c][e] = vf[c][e] = (__bf16)0.0f;
+    }
+  }
+  floatx16 dv[D / 32], dk[D / 32];
+#pragma unroll
+  for (int dl = 0; dl < D / 32; ++dl) dv[dl] = dk[dl] = floatx16{};
+
+  const int nq = (it.k1 - it.k0 + BQ - 1) / BQ;
+  PairStage<D> sq, sg;
+  float st_lse = 0.0f;
+  sq.load(Q + ho, rs, it.k0, it.k1, tid);
+  sg.load(dO + ho, rs, it.k0, it.k1, tid);
+  if (tid < 2 * BQ) {
+    const int row = it.k0 + (tid % BQ);
+    st_lse = row < it.k1 ? (tid < BQ ? LSE[(int64_t)it.head * Ns + row] * kLog2e
+                                     : delta[(int64_t)it.head * Ns + row])
+                         : 0.0f;
+  }
+  for (int t = 0; t < nq; ++t) {
+    const int qt0 = it.k0 + t * BQ;
+    __syncthreads();
+    sq.store(sm.q, sm.qt, tid);
+    sg.store(sm.g, sm.gt, tid);
+    if (tid < BQ) sm.lse2[tid] = st_lse;
+    else if (tid < 2 * BQ) sm.dl[tid - BQ] = st_lse;
+    __syncthreads();
+    if (t + 1 < nq) {
+      sq.load(Q + ho, rs, qt0 + BQ, it.k1, tid);
+      sg.load(dO + ho, rs, qt0 + BQ, it.k1, tid);
+      if (tid < 2 * BQ) {
+        const int row = qt0 + BQ + (tid % BQ);
+        st_lse = row < it.k1 ? (tid < BQ ? LSE[(int64_t)it.head * Ns + row] * kLog2e
+                                         : delta[(int64_t)it.head * Ns + row])
+                             : 0.0f;
+      }
+    }
+    const int qt1 = min(qt0 + BQ, it.k1);  // one past the last valid query
+    const bool active = wk0 < wk1 && !(causal && qt1 - 1 < wk0) &&
+                        !(window > 0 && qt0 - (wk1 - 1) >= window);
+    if (!active) continue;
+    const bool full = (qt0 + BQ <= it.k1) && (!causal || wk1 - 1 <= qt0) &&
+                      (window <= 0 || (qt0 + BQ - 1) - wk0 < window);
+#pragma unroll
+    for (int rho = 0; rho < BQ / 32; ++rho) {
+      floatx16 s = {}, dp = {};
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        s = mfma32x32x16(load_bf16x8(&sm.q[(32 * rho + l32) * RS + 16 * c + 8 * h]), kf[c], s);
+        dp = mfma32x32x16(load_bf16x8(&sm.g[(32 * rho + l32) * RS + 16 * c + 8 * h]), vf[c], dp);
+      }
+      // rows of s: query 32*rho + 8b + 4h + i of the tile; column: key kj
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int qr = 32 * rho + 8 * b + 4 * h;
+        const float4 l4 = *reinterpret_cast<const float4 *>(&sm.lse2[qr]);
+        const float4 d4 = *reinterpret_cast<const float4 *>(&sm.dl[qr]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * b + i;
+          float p = exp2f(fmaf(s[r], scale_log2, -lv[i]));
+          if (!full) {
+            const int qi = qt0 + qr + i;
+            const bool vis = qi < it.k1 && kok && (!causal || kj <= qi) &&
+                             (window <= 0 || qi - kj < window);
+            if (!vis) p = 0.0f;
+          }
+          s[r] = p;
+          dp[r] = p * (dp[r] - dv4[i]);
+        }
+      }
+      const bf16x8 pa[2] = {to_bf16x8(s, 0), to_bf16x8(s, 8)};
+      const bf16x8 da[2] = {to_bf16x8(dp, 0), to_bf16x8(dp, 8)};
+#pragma unroll
+      for (int dl = 0; dl < D / 32; ++dl)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int off = (32 * dl + l32) * TS + 32 * rho + 16 * m + 8 * h;
+          dv[dl] = mfma32x32x16(pa[m], load_bf16x8(&sm.gt[off]), dv[dl]);
+          dk[dl] = mfma32x32x16(da[m], load_bf16x8(&sm.qt[off]), dk[dl]);
+        }
+    }
+  }
+  // epilogue: accumulator rows are keys 8b + 4h + i of the wave, columns d
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = wk0 + 8 * (r / 4) + 4 * h + (r % 4);
+    if (key < it.q1) {
+#pragma unroll
+      for (int dl = 0; dl < D / 32; ++dl) {
+        const int64_t off = key * rs + ho + 32 * dl + l32;
+        dV[off] = dv[dl][r];
+        dK[off] = dk[dl][r] * scale;
+      }
+    }
+  }
+}
+
+// -------------------------------------------------------------------- dQ --
+
+template <int D>
+struct DqSmem {
+  static constexpr int RS = D + 8, TS = 72;
+  __bf16 k[kFwdBK * RS];
+  __bf16 v[kFwdBK * RS];
+  __bf16 kt[D * TS];
+};
+
+template <int D>
+__global__ __launch_bounds__(kFwdThreads, bwd_min_blocks<D>()) void dq_kernel(
+    const WorkItem *__restrict__ items, const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
+    const __bf16 *__restrict__ V, const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
+    const float *__restrict__ delta, float *__restrict__ dQ, int Hs, int64_t Ns, float scale,
+    float scale_log2, int causal, int window) {
+  constexpr int RS = DqSmem<D>::RS, TS = DqSmem<D>::TS, BK = kFwdBK;
+  __shared__ __attribute__((aligned(16))) DqSmem<D> sm;
+  const WorkItem it = items[blockIdx.x];  // queries [q0, q1), keys [k0, k1)
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int64_t rs = (int64_t)Hs * D;
+  const int64_t ho = (int64_t)it.head * D;
+  const int wq0 = it.q0 + 32 * w, wq1 = min(wq0 + 32, it.q1);
+  const int qi = wq0 + l32;
+  const bool qok = qi < it.q1;
+
+  bf16x8 qf[D / 16], gf[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    if (qok) {
+      qf[c] = load_bf16x8(Q + ho + qi * rs + 16 * c + 8 * h);
+      gf[c] = load_bf16x8(dO + ho + qi * rs + 16 * c + 8 * h);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[c][e] = gf[c][e] = (__bf16)0.0f;
+    }
+  }
+  const float lse2 = qok ? LSE[(int64_t)it.head * Ns + qi] * kLog2e : 0.0f;
+  const float dd = qok ? delta[(int64_t)it.head * Ns + qi] : 0.0f;
+  floatx16 dq[D / 32];
+#pragma unroll
+  for (int dl = 0; dl < D / 32; ++dl) dq[dl] = floatx16{};
+
+  const int nk = (it.k1 - it.k0 + BK - 1) / BK;
+  PairStage<D> sk, sv;
+  sk.load(K + ho, rs, it.k0, it.k1, tid);
+  sv.load(V + ho, rs, it.k0, it.k1, tid);
+  for (int t = 0; t < nk; ++t) {
+    const int kt0 = it.k0 + t * BK;
+    __syncthreads();
+    sk.store(sm.k, sm.kt, tid);
+    sv.store(sm.v, nullptr, tid);
+    __syncthreads();
+    if (t + 1 < nk) {
+      sk.load(K + ho, rs, kt0 + BK, it.k1, tid);
+      sv.load(V + ho, rs, kt0 + BK, it.k1, tid);
+    }
+    const bool active = wq0 < wq1 && !(causal && kt0 > wq1 - 1) &&
+                        !(window > 0 && wq0 - (kt0 + BK - 1) >= window);
+    if (!active) continue;
+    const bool full = (kt0 + BK <= it.k1) && (!causal || kt0 + BK - 1 <= wq0) &&
+                      (window <= 0 || (wq1 - 1) - kt0 < window);
+    floatx16 s[2], dp[2];
+#pragma unroll
+    for (int beta = 0; beta < 2; ++beta) {
+      s[beta] = dp[beta] = floatx16{};
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        const int off = (32 * beta + l32) * RS + 16 * c + 8 * h;
+        s[beta] = mfma32x32x16(load_bf16x8(&sm.k[off]), qf[c], s[beta]);
+        dp[beta] = mfma32x32x16(load_bf16x8(&sm.v[off]), gf[c], dp[beta]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = exp2f(fmaf(s[beta][r], scale_log2, -lse2));
+        if (!full) {
+          const int kj = kt0 + 32 * beta + 8 * (r / 4) + 4 * h + (r % 4);
+          const bool vis = kj < it.k1 && qok && (!causal || kj <= qi) &&
+                           (window <= 0 || qi - kj < window);
+          if (!vis) p = 0.0f;
+        }
+        dp[beta][r] = p * (dp[beta][r] - dd);
+      }
+    }
+#pragma unroll
+    for (int dl = 0; dl < D / 32; ++dl)
+#pragma unroll
+      for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const bf16x8 a = load_bf16x8(&sm.kt[(32 * dl + l32) * TS + 32 * beta + 16 * m + 8 * h]);
+          dq[dl] = mfma32x32x16(a, to_bf16x8(dp[beta], 8 * m), dq[dl]);
+        }
+  }
+  if (qok) {
+    float *row = dQ + qi * rs + ho;
+#pragma unroll
+    for (int dl = 0; dl < D / 32; ++dl)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        *reinterpret_cast<float4 *>(row + 32 * dl + 8 * b + 4 * h) =
+            make_float4(dq[dl][4 * b] * scale, dq[dl][4 * b + 1] * scale,
+                        dq[dl][4 * b + 2] * scale, dq[dl][4 * b + 3] * scale);
+  }
+}
+
+template <int D>
+hipError_t launch_typed(const attn_plan *p, const void *q, const void *k, const void *v,
+                        const void *o, const float *lse, const void *d_o, float *dq, float *dk,
+                        float *dv, hipStream_t stream) {
+  const int Hs = p->p.Hs;
+  const int64_t Ns = p->p.Ns;
+  const float scale = p->p.scale, scale_log2 = p->p.scale * kLog2e;
+  float *delta = reinterpret_cast<float *>(p->ws + p->off_delta);
+  const __bf16 *Q = static_cast<const __bf16 *>(q), *K = static_cast<const __bf16 *>(k);
+  const __bf16 *V = static_cast<const __bf16 *>(v), *O = static_cast<const __bf16 *>(o);
+  const __bf16 *G = static_cast<const __bf16 *>(d_o);
+  const int64_t rows = Ns * Hs;
+  hipLaunchKernelGGL((delta_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
+                     O, G, delta, Hs, Ns);
+  if (!p->bwd.empty())
+    hipLaunchKernelGGL((dkv_kernel<D>), dim3((unsigned)p->bwd.size()), dim3(kBwdThreads), 0,
+                       stream, reinterpret_cast<const WorkItem *>(p->ws + p->off_bwd), Q, K, V, G,
+                       lse, delta, dk, dv, Hs, Ns, scale, scale_log2, p->p.causal, p->p.window);
+  if (!p->fwd.empty())
+    hipLaunchKernelGGL((dq_kernel<D>), dim3((unsigned)p->fwd.size()), dim3(kFwdThreads), 0,
+                       stream, reinterpret_cast<const WorkItem *>(p->ws + p->off_fwd), Q, K, V, G,
+                       lse, delta, dq, Hs, Ns, scale, scale_log2, p->p.causal, p->p.window);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+attn_status launch_bwd(const attn_plan *p, const void *q, const void *k, const void *v,
+                       const void *o, const float *lse, const void *d_o, float *dq, float *dk,
+                       float *dv, hipStream_t stream) {
+  const hipError_t e = p->p.d == 64 ? launch_typed<64>(p, q, k, v, o, lse, d_o, dq, dk, dv, stream)
+                                    : launch_typed<128>(p, q, k, v, o, lse, d_o, dq, dk, dv, stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
 }  // namespace attn

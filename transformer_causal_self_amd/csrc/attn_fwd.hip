@@ -40,11 +40,6 @@ namespace {
 constexpr int BK = kFwdBK;  // key slots per step
 constexpr float kMinusBig = -1e30f;  // finite start value of the running max
 
-// Key position of key k (0..63 in a tile) inside the transposed V tile.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
-
 template <typename T, int D>
 struct Smem;
 template <int D>
@@ -108,7 +103,7 @@ struct Stage<__bf16, D> {
     for (int r = 0; r < VPT; ++r) {
       const int vi = tid + kFwdThreads * r;
       const int kp = vi % (BK / 2), c8 = vi / (BK / 2);
-      const int pos = vt_pos(2 * kp);  // even; key 2kp+1 lands at pos + 1
+      const int pos = perm16(2 * kp);  // even; key 2kp+1 lands at pos + 1
       const uint32_t a[4] = {vr[r][0].x, vr[r][0].y, vr[r][0].z, vr[r][0].w};
       const uint32_t b[4] = {vr[r][1].x, vr[r][1].y, vr[r][1].z, vr[r][1].w};
 #pragma unroll

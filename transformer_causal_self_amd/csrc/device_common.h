@@ -37,6 +37,16 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Position of row r (0..63) of a tile inside a transposed LDS copy whose rows
+// are read as the k operand of a 32x32x16 MFMA.  A 32x32 accumulator gives
+// lane half h the rows 8b + 4h + i (b = 0..3, i = 0..3); the k operand wants
+// 8 consecutive k per lane half.  Swapping bits 2 and 3 of the row index
+// inside each group of 16 makes the accumulator's rows 16m + 8b' + 4h + i
+// land at 16m + 8h + 4b' + i, i.e. eight contiguous positions per lane half.
+__device__ __forceinline__ int perm16(int r) {
+  return (r & ~0xC) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
 __device__ __forceinline__ floatx16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b,
                                                  const floatx16 &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
