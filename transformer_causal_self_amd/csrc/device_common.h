@@ -47,6 +47,24 @@ __device__ __forceinline__ int perm16(int r) {
   return (r & ~0xC) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// Raw buffer resource over [base, base + bytes): loads at byte offsets past
+// `bytes` return zeros, so ragged tile tails need no branch.  (Word 3 is the
+// gfx9-family raw-buffer format word.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// 2^x on the transcendental unit (v_exp_f32); results below the normal range
+// flush to zero, which is what softmax weights want.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
 __device__ __forceinline__ floatx16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b,
                                                  const floatx16 &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
