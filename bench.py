@@ -91,23 +91,36 @@ def cpu_baseline(w, inp, seconds):
     k = inp["k"].double().numpy()
     v = inp["v"].double().numpy()
 
-    def run(nrows):
-        rows = np.stack([rng.integers(0, Hs, nrows), rng.integers(0, Ns, nrows)], 1)
-        t0 = time.perf_counter()
-        qr = oracle.rope(q, cu, w.rope, w.rope_base, w.paired)
-        kr = oracle.rope(k, cu, w.rope, w.rope_base, w.paired)
-        oracle.attn_fwd_rows(qr, kr, v, cu, rows, w.paired, w.causal, w.window, w.scale)
-        dt = time.perf_counter() - t0
-        flops = sum(4.0 * w.head_dim * visible(int(s)) for s in rows[:, 1])
-        return dt, flops, nrows
+    def rows_sample(nrows):
+        return np.stack([rng.integers(0, Hs, nrows), rng.integers(0, Ns, nrows)], 1)
 
-    dt, fl, n = run(64)
-    n = int(min(Ns * Hs, max(64, 64 * seconds / max(dt, 1e-3))))
-    dt, fl, n = run(n)
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+    # calibrate: the RoPE of every token is a fixed cost, rows scale linearly
+    t0 = time.perf_counter()
+    qr = oracle.rope(q, cu, w.rope, w.rope_base, w.paired)
+    kr = oracle.rope(k, cu, w.rope, w.rope_base, w.paired)
+    t_rope = time.perf_counter() - t0
+    # each call has a fixed gather cost plus a per-row cost: two probe sizes
+    t_probe = []
+    for probe in (512, 2048):
+        t0 = time.perf_counter()
+        oracle.attn_fwd_rows(qr, kr, v, cu, rows_sample(probe), w.paired, w.causal, w.window,
+                             w.scale)
+        t_probe.append(time.perf_counter() - t0)
+    per_row = max((t_probe[1] - t_probe[0]) / 1536, 1e-7)
+    fixed = max(t_probe[0] - 512 * per_row, 0.0)
+    n = int(min(Ns * Hs, max(512, (seconds - t_rope - fixed) / per_row)))
+
+    rows = rows_sample(n)
+    t0 = time.perf_counter()
+    qr = oracle.rope(q, cu, w.rope, w.rope_base, w.paired)
+    kr = oracle.rope(k, cu, w.rope, w.rope_base, w.paired)
+    oracle.attn_fwd_rows(qr, kr, v, cu, rows, w.paired, w.causal, w.window, w.scale)
+    dt = time.perf_counter() - t0
+    flops = sum(4.0 * w.head_dim * visible(int(s)) for s in rows[:, 1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{n} random (head, query) rows of the forward of this workload plus the "
-                      f"RoPE of every token, fp64, {dt:.1f} s"}
+            "sample": f"{n} random (head, query) rows of this workload's forward (causal FLOPs "
+                      f"{flops / 1e9:.1f} GFLOP) plus the RoPE of every token, fp64, {dt:.1f} s"}
 
 
 def main():

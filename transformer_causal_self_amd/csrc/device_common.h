@@ -50,9 +50,11 @@ __device__ __forceinline__ int perm16(int r) {
 // Raw buffer resource over [base, base + bytes): loads at byte offsets past
 // `bytes` return zeros, so ragged tile tails need no branch.  (Word 3 is the
 // gfx9-family raw-buffer format word.)
+// Both arguments must be wave-uniform; readfirstlane states it, so the
+// descriptor lives in SGPRs (no waterfall loop around the load).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                           0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                           __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
 }
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
@@ -64,6 +66,19 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+// ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives element
+// (i % 4) of the 8-byte chunks addressed by lanes i/4, 4 + i/4, 8 + i/4 and
+// 12 + i/4 (in that order).  If lane 4e + g of the group addresses row
+// (r0 + e), columns (c0 + 4g .. c0 + 4g + 3) of a row-major bf16 tile, lane i
+// receives rows r0 .. r0 + 3 of column c0 + i: a transposed read.
+__device__ __forceinline__ uint2 lds_read_tr16(const __bf16 *p) {
+  const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p));
+  return __builtin_bit_cast(uint2, v);
+}
 
 __device__ __forceinline__ floatx16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b,
                                                  const floatx16 &c) {
