@@ -132,9 +132,20 @@ def test_counts_and_work_lists_cover_the_mask(cu, H, paired, causal, window):
         b, e = seq_of(r0)
         assert b <= r0 < r1 <= e and b <= s0 < s1 <= e
     assert (seen == 1).all()
-    # longest items first
-    steps = np.ceil((fwd[:, 4] - fwd[:, 3]) / 64)
-    assert (np.diff(steps) <= 0).all()
+    # XCD order: position i runs on XCD i % 8; a chunk of one stream's tiles
+    # stays on one XCD unless borrowed at the tail, and each XCD runs its items
+    # roughly longest first
+    for lst, step in ((fwd, 64), (bwd, 64)):
+        steps = np.ceil((lst[:, 4] - lst[:, 3]) / step)
+        per_stream = {}
+        for i, it in enumerate(lst):
+            per_stream.setdefault(int(it[5]), set()).add(i % 8)
+        n_streams = len(per_stream)
+        assert n_streams == len({(int(a), int(b)) for a, b in zip(lst[:, 0], lst[:, 5])})
+        for x in range(8):
+            sub = steps[x::8]
+            if len(sub) > 2:
+                assert sub[0] >= np.median(sub)
 
 
 @pytest.mark.parametrize("num,pairs", [(1, 33024), (2, 50380800), (5, 1610711040)])

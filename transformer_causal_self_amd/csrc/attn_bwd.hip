@@ -75,17 +75,18 @@ struct PairStage {
   static constexpr int UNITS = 32 * (D / 8);
   static constexpr int PT = UNITS / 256;  // units per thread
   uint4 r[PT][2];
+  // rows [t0, t0 + 64) of the head whose first slot is `base`; rows at or past
+  // `lim` read zero (the buffer resource ends there)
   __device__ __forceinline__ void load(const __bf16 *base, int64_t rs, int t0, int lim, int tid) {
+    const uint32_t rsb = (uint32_t)rs * 2u;
+    const auto rsrc = make_rsrc(base + (int64_t)t0 * rs, (uint32_t)max(0, min(lim - t0, 64)) * rsb);
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
       const int id = tid + 256 * u;
       const int rp = id % 32, c8 = id / 32;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int row = t0 + 2 * rp + e;
-        r[u][e] = row < lim ? *reinterpret_cast<const uint4 *>(base + row * rs + 8 * c8)
-                            : make_uint4(0, 0, 0, 0);
-      }
+      for (int e = 0; e < 2; ++e)
+        r[u][e] = buf_load16(rsrc, (uint32_t)(2 * rp + e) * rsb + 16u * c8);
     }
   }
   __device__ __forceinline__ void store(__bf16 *nat, __bf16 *tr, int tid) const {
@@ -125,7 +126,7 @@ constexpr int bwd_min_blocks() {
 // ---------------------------------------------------------------- dK, dV --
 
 template <int D>
-struct DkvSmem {
+struct DkvBuf {
   static constexpr int RS = D + 8, TS = 72, BQ = kBwdBQ;
   __bf16 q[BQ * RS];
   __bf16 g[BQ * RS];
@@ -133,6 +134,11 @@ struct DkvSmem {
   __bf16 gt[D * TS];
   float lse2[BQ];  // LSE * log2(e)
   float dl[BQ];    // D
+};
+template <int D>
+struct DkvSmem {
+  static constexpr int RS = DkvBuf<D>::RS, TS = DkvBuf<D>::TS;
+  DkvBuf<D> b[2];  // double buffered: one barrier per query tile
 };
 
 template <int D>
@@ -170,36 +176,33 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_blocks<D>()) void dkv_kernel(
   const int nq = (it.k1 - it.k0 + BQ - 1) / BQ;
   PairStage<D> sq, sg;
   float st_lse = 0.0f;
-  sq.load(Q + ho, rs, it.k0, it.k1, tid);
-  sg.load(dO + ho, rs, it.k0, it.k1, tid);
-  if (tid < 2 * BQ) {
-    const int row = it.k0 + (tid % BQ);
-    st_lse = row < it.k1 ? (tid < BQ ? LSE[(int64_t)it.head * Ns + row] * kLog2e
-                                     : delta[(int64_t)it.head * Ns + row])
-                         : 0.0f;
-  }
+  auto load_tile = [&](int q0) {
+    sq.load(Q + ho, rs, q0, it.k1, tid);
+    sg.load(dO + ho, rs, q0, it.k1, tid);
+    if (tid < 2 * BQ) {
+      const int row = q0 + (tid % BQ);
+      st_lse = row < it.k1 ? (tid < BQ ? LSE[(int64_t)it.head * Ns + row] * kLog2e
+                                       : delta[(int64_t)it.head * Ns + row])
+                           : 0.0f;
+    }
+  };
+  auto store_tile = [&](DkvBuf<D> &bf) {
+    sq.store(bf.q, bf.qt, tid);
+    sg.store(bf.g, bf.gt, tid);
+    if (tid < BQ) bf.lse2[tid] = st_lse;
+    else if (tid < 2 * BQ) bf.dl[tid - BQ] = st_lse;
+  };
+  load_tile(it.k0);
+  store_tile(sm.b[0]);
+  if (nq > 1) load_tile(it.k0 + BQ);
+  __syncthreads();
   for (int t = 0; t < nq; ++t) {
     const int qt0 = it.k0 + t * BQ;
-    __syncthreads();
-    sq.store(sm.q, sm.qt, tid);
-    sg.store(sm.g, sm.gt, tid);
-    if (tid < BQ) sm.lse2[tid] = st_lse;
-    else if (tid < 2 * BQ) sm.dl[tid - BQ] = st_lse;
-    __syncthreads();
-    if (t + 1 < nq) {
-      sq.load(Q + ho, rs, qt0 + BQ, it.k1, tid);
-      sg.load(dO + ho, rs, qt0 + BQ, it.k1, tid);
-      if (tid < 2 * BQ) {
-        const int row = qt0 + BQ + (tid % BQ);
-        st_lse = row < it.k1 ? (tid < BQ ? LSE[(int64_t)it.head * Ns + row] * kLog2e
-                                         : delta[(int64_t)it.head * Ns + row])
-                             : 0.0f;
-      }
-    }
+    const DkvBuf<D> &cur = sm.b[t & 1];
     const int qt1 = min(qt0 + BQ, it.k1);  // one past the last valid query
     const bool active = wk0 < wk1 && !(causal && qt1 - 1 < wk0) &&
                         !(window > 0 && qt0 - (wk1 - 1) >= window);
-    if (!active) continue;
+    if (active) {
     const bool full = (qt0 + BQ <= it.k1) && (!causal || wk1 - 1 <= qt0) &&
                       (window <= 0 || (qt0 + BQ - 1) - wk0 < window);
 #pragma unroll
@@ -207,20 +210,20 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_blocks<D>()) void dkv_kernel(
       floatx16 s = {}, dp = {};
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        s = mfma32x32x16(load_bf16x8(&sm.q[(32 * rho + l32) * RS + 16 * c + 8 * h]), kf[c], s);
-        dp = mfma32x32x16(load_bf16x8(&sm.g[(32 * rho + l32) * RS + 16 * c + 8 * h]), vf[c], dp);
+        s = mfma32x32x16(load_bf16x8(&cur.q[(32 * rho + l32) * RS + 16 * c + 8 * h]), kf[c], s);
+        dp = mfma32x32x16(load_bf16x8(&cur.g[(32 * rho + l32) * RS + 16 * c + 8 * h]), vf[c], dp);
       }
       // rows of s: query 32*rho + 8b + 4h + i of the tile; column: key kj
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int qr = 32 * rho + 8 * b + 4 * h;
-        const float4 l4 = *reinterpret_cast<const float4 *>(&sm.lse2[qr]);
-        const float4 d4 = *reinterpret_cast<const float4 *>(&sm.dl[qr]);
+        const float4 l4 = *reinterpret_cast<const float4 *>(&cur.lse2[qr]);
+        const float4 d4 = *reinterpret_cast<const float4 *>(&cur.dl[qr]);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * b + i;
-          float p = exp2f(fmaf(s[r], scale_log2, -lv[i]));
+          float p = fast_exp2(fmaf(s[r], scale_log2, -lv[i]));
           if (!full) {
             const int qi = qt0 + qr + i;
             const bool vis = qi < it.k1 && kok && (!causal || kj <= qi) &&
@@ -238,10 +241,16 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_blocks<D>()) void dkv_kernel(
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           const int off = (32 * dl + l32) * TS + 32 * rho + 16 * m + 8 * h;
-          dv[dl] = mfma32x32x16(pa[m], load_bf16x8(&sm.gt[off]), dv[dl]);
-          dk[dl] = mfma32x32x16(da[m], load_bf16x8(&sm.qt[off]), dk[dl]);
+          dv[dl] = mfma32x32x16(pa[m], load_bf16x8(&cur.gt[off]), dv[dl]);
+          dk[dl] = mfma32x32x16(da[m], load_bf16x8(&cur.qt[off]), dk[dl]);
         }
     }
+    }
+    if (t + 1 < nq) {
+      store_tile(sm.b[(t + 1) & 1]);
+      if (t + 2 < nq) load_tile(qt0 + 2 * BQ);
+    }
+    __syncthreads();
   }
   // epilogue: accumulator rows are keys 8b + 4h + i of the wave, columns d
 #pragma unroll
@@ -261,11 +270,16 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_blocks<D>()) void dkv_kernel(
 // -------------------------------------------------------------------- dQ --
 
 template <int D>
-struct DqSmem {
+struct DqBuf {
   static constexpr int RS = D + 8, TS = 72;
   __bf16 k[kFwdBK * RS];
   __bf16 v[kFwdBK * RS];
   __bf16 kt[D * TS];
+};
+template <int D>
+struct DqSmem {
+  static constexpr int RS = DqBuf<D>::RS, TS = DqBuf<D>::TS;
+  DqBuf<D> b[2];  // double buffered: one barrier per key tile
 };
 
 template <int D>
@@ -306,19 +320,19 @@ __global__ __launch_bounds__(kFwdThreads, bwd_min_blocks<D>()) void dq_kernel(
   PairStage<D> sk, sv;
   sk.load(K + ho, rs, it.k0, it.k1, tid);
   sv.load(V + ho, rs, it.k0, it.k1, tid);
+  sk.store(sm.b[0].k, sm.b[0].kt, tid);
+  sv.store(sm.b[0].v, nullptr, tid);
+  if (nk > 1) {
+    sk.load(K + ho, rs, it.k0 + BK, it.k1, tid);
+    sv.load(V + ho, rs, it.k0 + BK, it.k1, tid);
+  }
+  __syncthreads();
   for (int t = 0; t < nk; ++t) {
     const int kt0 = it.k0 + t * BK;
-    __syncthreads();
-    sk.store(sm.k, sm.kt, tid);
-    sv.store(sm.v, nullptr, tid);
-    __syncthreads();
-    if (t + 1 < nk) {
-      sk.load(K + ho, rs, kt0 + BK, it.k1, tid);
-      sv.load(V + ho, rs, kt0 + BK, it.k1, tid);
-    }
+    const DqBuf<D> &cur = sm.b[t & 1];
     const bool active = wq0 < wq1 && !(causal && kt0 > wq1 - 1) &&
                         !(window > 0 && wq0 - (kt0 + BK - 1) >= window);
-    if (!active) continue;
+    if (active) {
     const bool full = (kt0 + BK <= it.k1) && (!causal || kt0 + BK - 1 <= wq0) &&
                       (window <= 0 || (wq1 - 1) - kt0 < window);
     floatx16 s[2], dp[2];
@@ -328,12 +342,12 @@ __global__ __launch_bounds__(kFwdThreads, bwd_min_blocks<D>()) void dq_kernel(
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
         const int off = (32 * beta + l32) * RS + 16 * c + 8 * h;
-        s[beta] = mfma32x32x16(load_bf16x8(&sm.k[off]), qf[c], s[beta]);
-        dp[beta] = mfma32x32x16(load_bf16x8(&sm.v[off]), gf[c], dp[beta]);
+        s[beta] = mfma32x32x16(load_bf16x8(&cur.k[off]), qf[c], s[beta]);
+        dp[beta] = mfma32x32x16(load_bf16x8(&cur.v[off]), gf[c], dp[beta]);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = exp2f(fmaf(s[beta][r], scale_log2, -lse2));
+        float p = fast_exp2(fmaf(s[beta][r], scale_log2, -lse2));
         if (!full) {
           const int kj = kt0 + 32 * beta + 8 * (r / 4) + 4 * h + (r % 4);
           const bool vis = kj < it.k1 && qok && (!causal || kj <= qi) &&
@@ -349,9 +363,19 @@ __global__ __launch_bounds__(kFwdThreads, bwd_min_blocks<D>()) void dq_kernel(
       for (int beta = 0; beta < 2; ++beta)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const bf16x8 a = load_bf16x8(&sm.kt[(32 * dl + l32) * TS + 32 * beta + 16 * m + 8 * h]);
+          const bf16x8 a = load_bf16x8(&cur.kt[(32 * dl + l32) * TS + 32 * beta + 16 * m + 8 * h]);
           dq[dl] = mfma32x32x16(a, to_bf16x8(dp[beta], 8 * m), dq[dl]);
         }
+    }
+    if (t + 1 < nk) {
+      sk.store(sm.b[(t + 1) & 1].k, sm.b[(t + 1) & 1].kt, tid);
+      sv.store(sm.b[(t + 1) & 1].v, nullptr, tid);
+      if (t + 2 < nk) {
+        sk.load(K + ho, rs, kt0 + 2 * BK, it.k1, tid);
+        sv.load(V + ho, rs, kt0 + 2 * BK, it.k1, tid);
+      }
+    }
+    __syncthreads();
   }
   if (qok) {
     float *row = dQ + qi * rs + ho;

@@ -23,6 +23,8 @@ constexpr int kBwdBQ = 64;
 constexpr int kBwdThreads = 256;
 //   rotary: threads per block.
 constexpr int kRopeThreads = 256;
+// Work-list chunk: consecutive tiles of one head and sequence kept on one XCD.
+constexpr int kXcdChunk = 16;
 
 // One work item of the forward / dQ pass: attention head `head`, query slots
 // [q0, q1) inside one sequence, key slots [k0, k1) that any of those queries

@@ -33,8 +33,8 @@ int64_t visible_pairs_of(int64_t L, int causal, int window) {
 // can see it / be seen by it; appended as work items of `head`.
 // forward=true:  item rows are queries, span = visible keys.
 // forward=false: item rows are keys, span = queries that see them.
-void cut_items(std::vector<WorkItem> &out, int head, int64_t b, int64_t e, int tile, int causal,
-               int window, bool forward) {
+void cut_items(std::vector<WorkItem> &out, int head, int stream, int64_t b, int64_t e, int tile,
+               int causal, int window, bool forward) {
   for (int64_t r0 = b; r0 < e; r0 += tile) {
     const int64_t r1 = std::min<int64_t>(r0 + tile, e);
     int64_t s0, s1;
@@ -51,18 +51,75 @@ void cut_items(std::vector<WorkItem> &out, int head, int64_t b, int64_t e, int t
     w.q1 = (int32_t)r1;
     w.k0 = (int32_t)s0;
     w.k1 = (int32_t)s1;
+    w.pad0 = stream;
     out.push_back(w);
   }
 }
 
-// Longest first: items with more inner steps start earlier, so the tail of
-// the grid is made of short items (causal load balance).
-void sort_longest_first(std::vector<WorkItem> &v, int step) {
-  std::stable_sort(v.begin(), v.end(), [step](const WorkItem &a, const WorkItem &b) {
-    const int64_t na = (a.k1 - a.k0 + step - 1) / step;
-    const int64_t nb = (b.k1 - b.k0 + step - 1) / step;
-    return na > nb;
-  });
+int64_t steps_of(const WorkItem &w, int step) { return (w.k1 - w.k0 + step - 1) / step; }
+
+// Order the work list for the 8 XCDs of the chip.  Workgroup i runs on XCD
+// i mod 8, and each XCD has its own L2, so items that read the same keys (one
+// head of one sequence, nearby tiles) should share an XCD.  Items arrive in
+// (head, sequence, tile) order; runs of `chunk` consecutive tiles of one head
+// and sequence form a chunk.  Chunks go to XCDs by longest-processing-time
+// (largest chunk to the least loaded XCD); inside an XCD, chunks and the items
+// of a chunk run longest first (causal load balance); position 8j + x of the
+// final list is the j-th item of XCD x.  (pad0 carries the stream index.)
+void order_for_xcds(std::vector<WorkItem> &v, int step, int chunk) {
+  constexpr int kXcd = 8;
+  struct Chunk {
+    std::vector<WorkItem> items;
+    int64_t work = 0, longest = 0;
+  };
+  std::vector<Chunk> chunks;
+  for (size_t i = 0; i < v.size(); ++i) {
+    const bool same_run = i > 0 && v[i].pad0 == v[i - 1].pad0;
+    if (!same_run || (int)chunks.back().items.size() == chunk) chunks.emplace_back();
+    Chunk &c = chunks.back();
+    c.items.push_back(v[i]);
+    c.work += steps_of(v[i], step);
+    c.longest = std::max<int64_t>(c.longest, steps_of(v[i], step));
+  }
+  for (Chunk &c : chunks)
+    std::stable_sort(c.items.begin(), c.items.end(), [step](const WorkItem &a, const WorkItem &b) {
+      return steps_of(a, step) > steps_of(b, step);
+    });
+  std::vector<size_t> order(chunks.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](size_t a, size_t b) { return chunks[a].work > chunks[b].work; });
+  std::vector<std::vector<size_t>> xcd_chunks(kXcd);
+  int64_t load[kXcd] = {0};
+  for (size_t ci : order) {
+    const int x = (int)(std::min_element(load, load + kXcd) - load);
+    load[x] += chunks[ci].work;
+    xcd_chunks[x].push_back(ci);
+  }
+  std::vector<std::vector<WorkItem>> q(kXcd);
+  for (int x = 0; x < kXcd; ++x) {
+    std::stable_sort(xcd_chunks[x].begin(), xcd_chunks[x].end(),
+                     [&](size_t a, size_t b) { return chunks[a].longest > chunks[b].longest; });
+    for (size_t ci : xcd_chunks[x])
+      q[x].insert(q[x].end(), chunks[ci].items.begin(), chunks[ci].items.end());
+  }
+  // interleave; an XCD that runs out is refilled from the one with most work left
+  std::vector<size_t> head(kXcd, 0);
+  std::vector<int64_t> left(kXcd, 0);
+  for (int x = 0; x < kXcd; ++x)
+    for (const WorkItem &w : q[x]) left[x] += steps_of(w, step);
+  std::vector<WorkItem> out;
+  out.reserve(v.size());
+  while (out.size() < v.size()) {
+    const int x = (int)(out.size() % kXcd);
+    int src = x;
+    if (head[src] == q[src].size())
+      src = (int)(std::max_element(left.begin(), left.end()) - left.begin());
+    const WorkItem w = q[src][head[src]++];
+    left[src] -= steps_of(w, step);
+    out.push_back(w);
+  }
+  v.swap(out);
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -156,16 +213,18 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
 
     // Work lists and exact counts.
     int64_t pairs = 0;
+    int stream = 0;
     for (int j = 0; j < P.Hs; ++j)
       for (int s = 0; s < S; ++s) {
         const int64_t b = (int64_t)cu[s] * mult, e = (int64_t)cu[s + 1] * mult;
         if (e == b) continue;
         pairs += visible_pairs_of(e - b, P.causal, P.window);
-        cut_items(p->fwd, j, b, e, attn::kFwdBQ, P.causal, P.window, true);
-        cut_items(p->bwd, j, b, e, attn::kBwdBK, P.causal, P.window, false);
+        cut_items(p->fwd, j, stream, b, e, attn::kFwdBQ, P.causal, P.window, true);
+        cut_items(p->bwd, j, stream, b, e, attn::kBwdBK, P.causal, P.window, false);
+        ++stream;
       }
-    sort_longest_first(p->fwd, attn::kFwdBK);
-    sort_longest_first(p->bwd, attn::kBwdBQ);
+    order_for_xcds(p->fwd, attn::kFwdBK, attn::kXcdChunk);
+    order_for_xcds(p->bwd, attn::kBwdBQ, attn::kXcdChunk);
 
     const double elems = (double)P.N * P.H * P.d;
     const double es = P.dtype == ATTN_BF16 ? 2.0 : 4.0;

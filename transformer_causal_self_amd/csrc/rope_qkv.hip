@@ -12,10 +12,9 @@
 // dense output [N, H, d] is already the paired interleaved layout
 // [2N, H/2, d], so the interleave costs no extra pass.
 //
-// Work split: one thread owns one token and one chunk of PP consecutive pairs
-// and walks the H heads, so the chunk's cos/sin values (fp32, read from the
-// table, L2 resident) are loaded once per token and reused for every head of
-// Q and K.
+// Work split: one thread owns one token and two 16-byte units of every head
+// row, and walks the H heads, so its cos/sin values (fp32, read from the table,
+// L2 resident) are loaded once per token and reused for every head of Q and K.
 #include "attn_internal.h"
 #include "device_common.h"
 #include "launch.h"
@@ -66,99 +65,121 @@ __device__ __forceinline__ uint4 pack<float>(const float *f) {
                     __float_as_uint(f[3]));
 }
 
-// Rotate PP pairs of one head row.  HALF: pairs (c*PP + i, c*PP + i + D/2);
-// else pairs (2(c*PP + i), 2(c*PP + i) + 1).
+// Work split: a row of D elements is U = D / V sixteen-byte units (V elements
+// each).  Thread (token n, chunk c) owns units c and c + U/2 of every head row of
+// that token, so each load/store instruction of a wave covers whole 128-byte
+// lines.  Half-split pairs element i of unit c with element i of unit c + U/2;
+// adjacent pairs stay inside a unit.
 template <typename T, int D, bool HALF>
-__device__ __forceinline__ void rotate_row(const T *__restrict__ src, T *__restrict__ dst, int c,
-                                           const float *cs, const float *sn) {
-  constexpr int V = Vec<T>::kN;
-  constexpr int PP = V;  // pairs per thread
-  const uint4 *s4 = reinterpret_cast<const uint4 *>(src);
-  uint4 *d4 = reinterpret_cast<uint4 *>(dst);
-  float a[2 * V];
-  if (HALF) {
-    // first-half elements c*PP .. c*PP+PP, second half + D/2
-    const uint4 u0 = s4[c];
-    const uint4 u1 = s4[c + D / 2 / V];
-    unpack<T>(u0, a);
-    unpack<T>(u1, a + V);
-    float r[2 * V];
-#pragma unroll
-    for (int i = 0; i < PP; ++i) {
-      const float x = a[i], y = a[V + i];
-      r[i] = fmaf(x, cs[i], -y * sn[i]);
-      r[V + i] = fmaf(y, cs[i], x * sn[i]);
-    }
-    d4[c] = pack<T>(r);
-    d4[c + D / 2 / V] = pack<T>(r + V);
-  } else {
-    // 2*PP consecutive elements = PP adjacent pairs
-    const uint4 u0 = s4[2 * c];
-    const uint4 u1 = s4[2 * c + 1];
-    unpack<T>(u0, a);
-    unpack<T>(u1, a + V);
-    float r[2 * V];
-#pragma unroll
-    for (int i = 0; i < PP; ++i) {
-      const float x = a[2 * i], y = a[2 * i + 1];
-      r[2 * i] = fmaf(x, cs[i], -y * sn[i]);
-      r[2 * i + 1] = fmaf(y, cs[i], x * sn[i]);
-    }
-    d4[2 * c] = pack<T>(r);
-    d4[2 * c + 1] = pack<T>(r + V);
+struct RopeChunk {
+  static constexpr int V = Vec<T>::kN;
+  static constexpr int U = D / V;
+  // a thread rotates V pairs: V half-split pairs across its two units, or V/2
+  // adjacent pairs inside each unit.  Table column of its pair i: half-split
+  // c*V + i; adjacent u*V/2 + i' for unit u = c (i < V/2) or c + U/2.
+  static constexpr int NP = V;
+  __device__ static __forceinline__ int col(int c, int i) {
+    if (HALF) return c * V + i;
+    return (i < V / 2) ? c * (V / 2) + i : (c + U / 2) * (V / 2) + (i - V / 2);
   }
-}
+  __device__ static __forceinline__ void rotate(const uint4 &u0, const uint4 &u1, const float *cs,
+                                                const float *sn, uint4 &r0, uint4 &r1) {
+    float a[V], b[V], x[V], y[V];
+    unpack<T>(u0, a);
+    unpack<T>(u1, b);
+    if (HALF) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        x[i] = fmaf(a[i], cs[i], -b[i] * sn[i]);
+        y[i] = fmaf(b[i], cs[i], a[i] * sn[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < V / 2; ++i) {
+        x[2 * i] = fmaf(a[2 * i], cs[i], -a[2 * i + 1] * sn[i]);
+        x[2 * i + 1] = fmaf(a[2 * i + 1], cs[i], a[2 * i] * sn[i]);
+        const int j = V / 2 + i;
+        y[2 * i] = fmaf(b[2 * i], cs[j], -b[2 * i + 1] * sn[j]);
+        y[2 * i + 1] = fmaf(b[2 * i + 1], cs[j], b[2 * i] * sn[j]);
+      }
+    }
+    r0 = pack<T>(x);
+    r1 = pack<T>(y);
+  }
+};
 
 template <typename T, int D, bool HALF, bool PAIRED>
 __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
-    const T *__restrict__ q, int64_t qs, const T *__restrict__ k, int64_t ks,
-    const T *__restrict__ v, int64_t vs, T *__restrict__ qo, T *__restrict__ ko,
-    T *__restrict__ vo, const int32_t *__restrict__ tok_pos, const float *__restrict__ tcos,
-    const float *__restrict__ tsin, int64_t N, int H) {
-  constexpr int V = Vec<T>::kN;
-  constexpr int PP = V;
-  constexpr int C = D / 2 / PP;  // chunks per head row
+    const T *q, int64_t qs, const T *k, int64_t ks, const T *__restrict__ v, int64_t vs, T *qo,
+    T *ko, T *__restrict__ vo, const int32_t *__restrict__ tok_pos,
+    const float *__restrict__ tcos, const float *__restrict__ tsin, int64_t N, int H) {
+  using RC = RopeChunk<T, D, HALF>;
+  constexpr int V = RC::V, U = RC::U, NP = RC::NP;
   const int64_t gid = (int64_t)blockIdx.x * kRopeThreads + threadIdx.x;
-  const int64_t n = gid / C;
-  const int c = (int)(gid % C);
+  const int64_t n = gid / (U / 2);
+  const int c = (int)(gid % (U / 2));
   if (n >= N) return;
   const int t = tok_pos[n];
-  // cos/sin of the chunk's PP pairs at the (one or two) positions used here.
-  float cs[2][PP], sn[2][PP];
+  float cs[2][NP], sn[2][NP];
 #pragma unroll
   for (int par = 0; par < (PAIRED ? 2 : 1); ++par) {
-    const int pos = PAIRED ? 2 * t + par : t;
-    const float4 *c4 = reinterpret_cast<const float4 *>(tcos + (int64_t)pos * (D / 2) + c * PP);
-    const float4 *s4 = reinterpret_cast<const float4 *>(tsin + (int64_t)pos * (D / 2) + c * PP);
+    const int64_t pos = PAIRED ? 2 * t + par : t;
+    const float *cr = tcos + pos * (D / 2), *sr = tsin + pos * (D / 2);
 #pragma unroll
-    for (int i = 0; i < PP / 4; ++i) {
-      const float4 cc = c4[i], ss = s4[i];
-      cs[par][4 * i] = cc.x;
-      cs[par][4 * i + 1] = cc.y;
-      cs[par][4 * i + 2] = cc.z;
-      cs[par][4 * i + 3] = cc.w;
-      sn[par][4 * i] = ss.x;
-      sn[par][4 * i + 1] = ss.y;
-      sn[par][4 * i + 2] = ss.z;
-      sn[par][4 * i + 3] = ss.w;
+    for (int i = 0; i < NP; ++i) {
+      cs[par][i] = cr[RC::col(c, i)];
+      sn[par][i] = sr[RC::col(c, i)];
     }
   }
   const int64_t row = (int64_t)H * D;
-  for (int h = 0; h < H; ++h) {
+  const uint4 *q4 = reinterpret_cast<const uint4 *>(q + n * qs);
+  const uint4 *k4 = reinterpret_cast<const uint4 *>(k + n * ks);
+  uint4 *qo4 = reinterpret_cast<uint4 *>(qo + n * row);
+  uint4 *ko4 = reinterpret_cast<uint4 *>(ko + n * row);
+  int h = 0;
+  // two heads per step: eight 16-byte loads in flight before any store
+  for (; h + 1 < H; h += 2) {
+    uint4 in[2][2][2];  // [head][q/k][unit]
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int base = (h + e) * U;
+      in[e][0][0] = q4[base + c];
+      in[e][0][1] = q4[base + c + U / 2];
+      in[e][1][0] = k4[base + c];
+      in[e][1][1] = k4[base + c + U / 2];
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int par = PAIRED ? ((h + e) & 1) : 0;
+      const int base = (h + e) * U;
+      uint4 r0, r1;
+      RC::rotate(in[e][0][0], in[e][0][1], cs[par], sn[par], r0, r1);
+      qo4[base + c] = r0;
+      qo4[base + c + U / 2] = r1;
+      RC::rotate(in[e][1][0], in[e][1][1], cs[par], sn[par], r0, r1);
+      ko4[base + c] = r0;
+      ko4[base + c + U / 2] = r1;
+    }
+  }
+  if (h < H) {
     const int par = PAIRED ? (h & 1) : 0;
-    rotate_row<T, D, HALF>(q + n * qs + h * D, qo + n * row + h * D, c, cs[par], sn[par]);
-    rotate_row<T, D, HALF>(k + n * ks + h * D, ko + n * row + h * D, c, cs[par], sn[par]);
-    if (vo) {
-      // dense copy of this thread's two 16-byte pieces of V
-      const uint4 *s4 = reinterpret_cast<const uint4 *>(v + n * vs + h * D);
-      uint4 *d4 = reinterpret_cast<uint4 *>(vo + n * row + h * D);
-      if (HALF) {
-        d4[c] = s4[c];
-        d4[c + D / 2 / V] = s4[c + D / 2 / V];
-      } else {
-        d4[2 * c] = s4[2 * c];
-        d4[2 * c + 1] = s4[2 * c + 1];
-      }
+    const int base = h * U;
+    const uint4 a0 = q4[base + c], a1 = q4[base + c + U / 2];
+    const uint4 b0 = k4[base + c], b1 = k4[base + c + U / 2];
+    uint4 r0, r1;
+    RC::rotate(a0, a1, cs[par], sn[par], r0, r1);
+    qo4[base + c] = r0;
+    qo4[base + c + U / 2] = r1;
+    RC::rotate(b0, b1, cs[par], sn[par], r0, r1);
+    ko4[base + c] = r0;
+    ko4[base + c + U / 2] = r1;
+  }
+  if (vo) {
+    const uint4 *v4 = reinterpret_cast<const uint4 *>(v + n * vs);
+    uint4 *vo4 = reinterpret_cast<uint4 *>(vo + n * row);
+    for (int hh = 0; hh < H; ++hh) {
+      vo4[hh * U + c] = v4[hh * U + c];
+      vo4[hh * U + c + U / 2] = v4[hh * U + c + U / 2];
     }
   }
 }
@@ -167,7 +188,7 @@ template <typename T, int D>
 hipError_t launch_typed(const attn_plan *p, const void *q, int64_t qs, const void *k, int64_t ks,
                         const void *v, int64_t vs, void *qo, void *ko, void *vo,
                         hipStream_t stream) {
-  constexpr int C = D / 2 / Vec<T>::kN;
+  constexpr int C = D / Vec<T>::kN / 2;  // threads per token
   const int64_t N = p->p.N;
   const int64_t threads = N * C;
   const dim3 grid((unsigned)((threads + kRopeThreads - 1) / kRopeThreads));
