@@ -319,13 +319,46 @@ struct StageBF {
   }
 };
 
+constexpr float kOverflow = 18446744073709551616.0f;  // 2^64
+
+// Causal / window / key-range mask of one 64-key tile for this lane's query;
+// the key of s[beta][r] is kt0 + 4h + 32 beta + 8 (r / 4) + r % 4.
+__device__ __forceinline__ void mask_tile(floatx16 (&s)[2], int kt0, int k1, int qi, int h,
+                                          int causal, int window) {
+  const int kb = kt0 + 4 * h;
+  const int hi = (causal ? min(k1 - 1, qi) : k1 - 1) - kb;
+  const int lo = window > 0 ? qi - window + 1 - kb : -(1 << 30);
+#pragma unroll
+  for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rel = 32 * beta + 8 * (r / 4) + (r % 4);
+      if (rel > hi || rel < lo) s[beta][r] = -INFINITY;
+    }
+}
+
+// S^T of the staged K tile again (rare path).
+template <int D>
+__device__ __forceinline__ void scores_again(const __bf16 *ks, const bf16x8 (&qf)[D / 16], int l32,
+                                          int h, floatx16 (&s)[2]) {
+  constexpr int KS = D + 8;
+  s[0] = floatx16{};
+  s[1] = floatx16{};
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    s[0] = mfma32x32x16(*reinterpret_cast<const bf16x8 *>(&ks[l32 * KS + 16 * c + 8 * h]), qf[c],
+                        s[0]);
+    s[1] = mfma32x32x16(*reinterpret_cast<const bf16x8 *>(&ks[(32 + l32) * KS + 16 * c + 8 * h]),
+                        qf[c], s[1]);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(
     const WorkItem *__restrict__ items, const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const __bf16 *__restrict__ V, __bf16 *__restrict__ O, float *__restrict__ LSE, int Hs,
     int64_t Ns, float scale, float scale_log2, int causal, int window) {
   constexpr int KS = SmemBF<D>::KS, VS = SmemBF<D>::VS;
-  constexpr float kRescale = 8.0f;  // move the running max only past 2^8 growth
   __shared__ __attribute__((aligned(16))) SmemBF<D> sm;
   const WorkItem it = items[blockIdx.x];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -356,6 +389,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(
   float m = kMinusBig;  // running max of raw scores (the exponent's reference)
   float mb = m * scale_log2;
   float l = 0.0f;       // this lane's part of the running sum
+  bool first = true;    // no active tile seen yet (wave-uniform)
 
   const int nk = (it.k1 - it.k0 + BK - 1) / BK;
   StageBF<D> st;
@@ -390,26 +424,34 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(
         s[0] = mfma32x32x16(a[0][c], qf[c], s[0]);
         s[1] = mfma32x32x16(a[1][c], qf[c], s[1]);
       }
-      if (!full) {
-        // key of s[beta][r] = kt0 + 4h + 32 beta + 8 (r / 4) + r % 4
-        const int kb = kt0 + 4 * h;
-        const int hi = (causal ? min(it.k1 - 1, qi) : it.k1 - 1) - kb;
-        const int lo = window > 0 ? qi - window + 1 - kb : -(1 << 30);
+      if (!full) mask_tile(s, kt0, it.k1, qi, h, causal, window);
+      // weights against the current reference max; the row max is only taken
+      // on the wave's first tile and when some weight would exceed 2^64 (a
+      // score more than 64 above the reference in the exp2 domain)
+      float ls = 0.0f;
+      bool need_max = first;
+      if (!need_max) {
 #pragma unroll
         for (int beta = 0; beta < 2; ++beta)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int rel = 32 * beta + 8 * (r / 4) + (r % 4);
-            if (rel > hi || rel < lo) s[beta][r] = -INFINITY;
+            const float pv = fast_exp2(fmaf(s[beta][r], scale_log2, -mb));
+            s[beta][r] = pv;
+            ls += pv;
           }
+        need_max = wave_any(!(ls <= kOverflow));
+        if (need_max) {  // rare: the raw scores were overwritten, form them again
+          scores_again<D>(ks, qf, l32, h, s);
+          if (!full) mask_tile(s, kt0, it.k1, qi, h, causal, window);
+        }
       }
-      float mx = s[0][0];
+      if (need_max) {
+        float mx = s[0][0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-      mx = halves_max(mx);
-      if (wave_any(mx * scale_log2 > mb + kRescale)) {
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+        mx = halves_max(mx);
         const float m_new = fmaxf(m, mx);
         const float alpha = fast_exp2((m - m_new) * scale_log2);
         m = m_new;
@@ -419,17 +461,18 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(
         for (int dl = 0; dl < D / 32; ++dl)
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[dl][r] *= alpha;
+        ls = 0.0f;
+#pragma unroll
+        for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float pv = fast_exp2(fmaf(s[beta][r], scale_log2, -mb));
+            s[beta][r] = pv;
+            ls += pv;
+          }
       }
-      float ls = 0.0f;
-#pragma unroll
-      for (int beta = 0; beta < 2; ++beta)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = fast_exp2(fmaf(s[beta][r], scale_log2, -mb));
-          s[beta][r] = pv;
-          ls += pv;
-        }
       l += ls;
+      first = false;
       bf16x8 pf[2][2];
 #pragma unroll
       for (int beta = 0; beta < 2; ++beta)
