@@ -205,6 +205,10 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_blocks<D>()) void dkv_kernel(
     if (active) {
     const bool full = (qt0 + BQ <= it.k1) && (!causal || wk1 - 1 <= qt0) &&
                       (window <= 0 || (qt0 + BQ - 1) - wk0 < window);
+    // query rows (tile-relative) that see this lane's key: [qlo, qhi]; the
+    // lane's key itself may be past the item end -- its column is never stored
+    const int qlo = causal ? kj - qt0 : -(1 << 30);
+    const int qhi = min(it.k1 - 1, window > 0 ? kj + window - 1 : (1 << 30)) - qt0;
 #pragma unroll
     for (int rho = 0; rho < BQ / 32; ++rho) {
       floatx16 s = {}, dp = {};
@@ -224,12 +228,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_blocks<D>()) void dkv_kernel(
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * b + i;
           float p = fast_exp2(fmaf(s[r], scale_log2, -lv[i]));
-          if (!full) {
-            const int qi = qt0 + qr + i;
-            const bool vis = qi < it.k1 && kok && (!causal || kj <= qi) &&
-                             (window <= 0 || qi - kj < window);
-            if (!vis) p = 0.0f;
-          }
+          if (!full && (qr + i > qhi || qr + i < qlo)) p = 0.0f;
           s[r] = p;
           dp[r] = p * (dp[r] - dv4[i]);
         }
@@ -335,6 +334,11 @@ __global__ __launch_bounds__(kFwdThreads, bwd_min_blocks<D>()) void dq_kernel(
     if (active) {
     const bool full = (kt0 + BK <= it.k1) && (!causal || kt0 + BK - 1 <= wq0) &&
                       (window <= 0 || (wq1 - 1) - kt0 < window);
+    // keys (relative to kt0 + 4h) this lane's query sees: [klo, khi]; the
+    // lane's query may be past the item end -- its row is never stored
+    const int kb = kt0 + 4 * h;
+    const int khi = (causal ? min(it.k1 - 1, qi) : it.k1 - 1) - kb;
+    const int klo = window > 0 ? qi - window + 1 - kb : -(1 << 30);
     floatx16 s[2], dp[2];
 #pragma unroll
     for (int beta = 0; beta < 2; ++beta) {
@@ -348,12 +352,8 @@ __global__ __launch_bounds__(kFwdThreads, bwd_min_blocks<D>()) void dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(fmaf(s[beta][r], scale_log2, -lse2));
-        if (!full) {
-          const int kj = kt0 + 32 * beta + 8 * (r / 4) + 4 * h + (r % 4);
-          const bool vis = kj < it.k1 && qok && (!causal || kj <= qi) &&
-                           (window <= 0 || qi - kj < window);
-          if (!vis) p = 0.0f;
-        }
+        const int rel = 32 * beta + 8 * (r / 4) + (r % 4);
+        if (!full && (rel > khi || rel < klo)) p = 0.0f;
         dp[beta][r] = p * (dp[beta][r] - dd);
       }
     }
