@@ -132,13 +132,16 @@ attn_status attn_plan_stats(const attn_plan *plan, attn_plan_info *info);
 
 /*
  * Introspection of the tile work lists (host only), for testing and
- * scheduling analysis.  which = 0: forward items; which = 1: backward key-tile
- * items.  Each item is 8 int32: {attention head, r0, r1, s0, s1, stream, 0, 0}
+ * scheduling analysis.  which = 0: forward items (256 query slots each for
+ * bf16, 128 for fp32); which = 1: backward key-tile items (128 key slots);
+ * which = 2: backward dQ items (128 query slots).  The backward lists are
+ * empty for fp32 problems.
+ * Each item is 8 int32: {attention head, r0, r1, s0, s1, stream, 0, 0}
  * where stream numbers the (attention head, sequence) pairs.  The list order
  * is the launch order: item i runs as workgroup i, on XCD i mod 8; items of one
  * stream and nearby tiles share an XCD (and its L2), longest first within it.
- * Forward: query slots [r0, r1) of one sequence and the key slots [s0, s1)
- * any of them may see.  Backward: key slots [r0, r1) and the query slots
+ * Forward and dQ: query slots [r0, r1) of one sequence and the key slots
+ * [s0, s1) any of them may see.  Backward: key slots [r0, r1) and the query slots
  * [s0, s1) that may see them.  Copies min(count, capacity) items into out
  * (out may be NULL when capacity is 0) and stores the total count in *count.
  */

@@ -77,6 +77,27 @@ def test_empty_problem_is_valid():
     assert p.workspace_bytes >= 256
 
 
+def test_item_sizes_follow_the_dtype():
+    # bf16: 256-query forward items, 128-query dQ items, 128-key dK/dV items;
+    # fp32 (no backward): 128-query forward items and empty backward lists
+    cu = [0, 700]
+    pb = plan(num_tokens=700, cu_seqlens=cu)
+    pf = plan(num_tokens=700, cu_seqlens=cu, dtype="fp32")
+    assert (np.diff(pb.work_items(0)[:, 1:3], axis=1).max()) == 256
+    assert (np.diff(pb.work_items(2)[:, 1:3], axis=1).max()) == 128
+    assert (np.diff(pb.work_items(1)[:, 1:3], axis=1).max()) == 128
+    assert (np.diff(pf.work_items(0)[:, 1:3], axis=1).max()) == 128
+    # a short window keeps 128-query forward items (a longer one does not)
+    assert np.diff(plan(num_tokens=700, cu_seqlens=cu, window=512).work_items(0)[:, 1:3],
+                   axis=1).max() == 128
+    assert np.diff(plan(num_tokens=700, cu_seqlens=cu, window=513).work_items(0)[:, 1:3],
+                   axis=1).max() == 256
+    assert len(pf.work_items(1)) == 0 and len(pf.work_items(2)) == 0
+    for bad in (-1, 3):
+        with pytest.raises(tca.AttnError):
+            pb.work_items(bad)
+
+
 def dense_pairs(cu, mult, causal, window):
     return int(brute.dense_mask(list(cu), mult, causal, window).sum())
 
@@ -106,21 +127,24 @@ def test_counts_and_work_lists_cover_the_mask(cu, H, paired, causal, window):
     assert p.info["slots"] == N * mult and p.info["attn_heads"] == Hs
     fwd = p.work_items(0)
     bwd = p.work_items(1)
-    # forward: every (head, query) row exactly once; its visible keys inside [k0, k1)
+    dq = p.work_items(2)
+    # forward (256-query items for bf16) and dQ (128-query items): every
+    # (head, query) row exactly once; its visible keys inside [k0, k1)
     bounds = np.array(cu) * mult
     def seq_of(slot):
         s = np.searchsorted(bounds, slot, side="right") - 1
         return bounds[s], bounds[s + 1]
-    seen = np.zeros((Hs, N * mult), dtype=int)
-    for head, q0, q1, k0, k1, *_ in fwd:
-        assert 0 < q1 - q0 <= 128
-        seen[head, q0:q1] += 1
-        rows = mask[q0:q1]
-        cols = np.nonzero(rows.any(axis=0))[0]
-        assert cols.min() >= k0 and cols.max() < k1
-        b, e = seq_of(q0)          # the item stays inside one sequence
-        assert b <= q0 < q1 <= e and b <= k0 < k1 <= e
-    assert (seen == 1).all()
+    for lst, rows_max in ((fwd, 256), (dq, 128)):
+        seen = np.zeros((Hs, N * mult), dtype=int)
+        for head, q0, q1, k0, k1, *_ in lst:
+            assert 0 < q1 - q0 <= rows_max
+            seen[head, q0:q1] += 1
+            rows = mask[q0:q1]
+            cols = np.nonzero(rows.any(axis=0))[0]
+            assert cols.min() >= k0 and cols.max() < k1
+            b, e = seq_of(q0)          # the item stays inside one sequence
+            assert b <= q0 < q1 <= e and b <= k0 < k1 <= e
+        assert (seen == 1).all()
     # backward: every (head, key) column exactly once; the queries that see it in [s0, s1)
     seen = np.zeros((Hs, N * mult), dtype=int)
     for head, r0, r1, s0, s1, *_ in bwd:
@@ -135,7 +159,7 @@ def test_counts_and_work_lists_cover_the_mask(cu, H, paired, causal, window):
     # XCD order: position i runs on XCD i % 8; a chunk of one stream's tiles
     # stays on one XCD unless borrowed at the tail, and each XCD runs its items
     # roughly longest first
-    for lst, step in ((fwd, 64), (bwd, 64)):
+    for lst, step in ((fwd, 64), (bwd, 64), (dq, 64)):
         steps = np.ceil((lst[:, 4] - lst[:, 3]) / step)
         per_stream = {}
         for i, it in enumerate(lst):

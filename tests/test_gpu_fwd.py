@@ -176,6 +176,9 @@ EDGE = [
     ("fp32 varlen window", 3, 128, wl.DTYPE_FP32, [0, 70, 200, 333], 0, 100, 2),
     ("fp32 paired", 4, 64, wl.DTYPE_FP32, [0, 129, 200], 1, 0, 1),
     ("single token", 2, 64, wl.DTYPE_BF16, [0, 1], 0, 0, 1),
+    # windows past 512 slots run the 256-query items of the bf16 kernel
+    ("window 513", 2, 64, wl.DTYPE_BF16, [0, 1100], 0, 513, 1),
+    ("paired H2 window 600", 2, 128, wl.DTYPE_BF16, [0, 300, 1000], 1, 600, 2),
 ]
 
 

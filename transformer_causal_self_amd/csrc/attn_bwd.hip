@@ -282,7 +282,7 @@ struct DqSmem {
 };
 
 template <int D>
-__global__ __launch_bounds__(kFwdThreads, bwd_min_blocks<D>()) void dq_kernel(
+__global__ __launch_bounds__(kDqThreads, bwd_min_blocks<D>()) void dq_kernel(
     const WorkItem *__restrict__ items, const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const __bf16 *__restrict__ V, const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
     const float *__restrict__ delta, float *__restrict__ dQ, int Hs, int64_t Ns, float scale,
@@ -407,9 +407,9 @@ hipError_t launch_typed(const attn_plan *p, const void *q, const void *k, const 
     hipLaunchKernelGGL((dkv_kernel<D>), dim3((unsigned)p->bwd.size()), dim3(kBwdThreads), 0,
                        stream, reinterpret_cast<const WorkItem *>(p->ws + p->off_bwd), Q, K, V, G,
                        lse, delta, dk, dv, Hs, Ns, scale, scale_log2, p->p.causal, p->p.window);
-  if (!p->fwd.empty())
-    hipLaunchKernelGGL((dq_kernel<D>), dim3((unsigned)p->fwd.size()), dim3(kFwdThreads), 0,
-                       stream, reinterpret_cast<const WorkItem *>(p->ws + p->off_fwd), Q, K, V, G,
+  if (!p->dq.empty())
+    hipLaunchKernelGGL((dq_kernel<D>), dim3((unsigned)p->dq.size()), dim3(kDqThreads), 0,
+                       stream, reinterpret_cast<const WorkItem *>(p->ws + p->off_dq), Q, K, V, G,
                        lse, delta, dq, Hs, Ns, scale, scale_log2, p->p.causal, p->p.window);
   return hipGetLastError();
 }

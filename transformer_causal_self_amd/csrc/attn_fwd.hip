@@ -10,8 +10,10 @@
 // ("Upgrading a textbook decoder", juejin.cn, section 4, FlashAttention: the
 // tiling changes where the result is computed, not the result).
 //
-// gfx950 mapping (one work item = one block of 4 waves = 128 query slots of
-// one attention head; each wave owns 32 query slots):
+// gfx950 mapping (one work item = one block of 8 waves = 256 query slots of
+// one attention head for bf16, 4 waves = 128 slots for fp32 and for windows of
+// at most 512 slots; each wave owns 32 query slots, and every K/V tile staged
+// in LDS serves the whole block):
 //   * Each wave holds its 32 queries as the B operand of
 //     v_mfma_f32_32x32x16_bf16 for the whole item (registers).
 //   * K tiles of 64 key slots are staged in LDS row-major; V tiles are staged
@@ -56,7 +58,7 @@ struct Stage;
 
 template <int D>
 struct Stage<float, D> {
-  static constexpr int PT = BK * D / 4 / kFwdThreads;  // float4 chunks per thread (K and V)
+  static constexpr int PT = BK * D / 4 / kFwdThreadsF32;  // float4 chunks per thread (K and V)
   float4 kr[PT];
   float4 vr[PT];
 
@@ -64,7 +66,7 @@ struct Stage<float, D> {
                                        int k1, int tid) {
 #pragma unroll
     for (int r = 0; r < PT; ++r) {
-      const int ci = tid + kFwdThreads * r;
+      const int ci = tid + kFwdThreadsF32 * r;
       const int key = ci / (D / 4), c4 = ci % (D / 4);
       const int slot = kt0 + key;
       const bool ok = slot < k1;
@@ -79,7 +81,7 @@ struct Stage<float, D> {
     constexpr int KS = Smem<float, D>::KS, VS = Smem<float, D>::VS;
 #pragma unroll
     for (int r = 0; r < PT; ++r) {
-      const int ci = tid + kFwdThreads * r;
+      const int ci = tid + kFwdThreadsF32 * r;
       const int key = ci / (D / 4), c4 = ci % (D / 4);
       float *kd = &sm.k[key * KS + 4 * c4];
       kd[0] = kr[r].x;
@@ -148,7 +150,7 @@ constexpr int fwd_min_blocks() {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kFwdThreads, fwd_min_blocks<T>()) void fwd_kernel(
+__global__ __launch_bounds__(kFwdThreadsF32, fwd_min_blocks<T>()) void fwd_kernel(
     const WorkItem *__restrict__ items, const T *__restrict__ Q, const T *__restrict__ K,
     const T *__restrict__ V, T *__restrict__ O, float *__restrict__ LSE, int Hs, int64_t Ns,
     float scale, float scale_log2, int causal, int window) {
@@ -268,10 +270,12 @@ struct SmemBF {
   __bf16 vt[2][D * VS];
 };
 
-template <int D>
+template <int D, int NT>
 struct StageBF {
-  static constexpr int KPT = BK * D / 8 / kFwdThreads;          // 16-byte K chunks per thread
-  static constexpr int VPT = (BK / 2) * (D / 8) / kFwdThreads;  // (key pair, 8 features) units
+  static constexpr int KPT = BK * D / 8 / NT;  // 16-byte K chunks per thread
+  static_assert(KPT >= 1 && BK * D / 8 % NT == 0, "K staging split");
+  static constexpr int VU = (BK / 2) * (D / 8);  // (key pair, 8 features) units per tile
+  static constexpr int VPT = (VU + NT - 1) / NT;
   uint4 kr[KPT];
   uint4 vr[VPT][2];
 
@@ -283,12 +287,13 @@ struct StageBF {
     const auto rv = make_rsrc(Vt, bytes);
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
-      const int ci = tid + kFwdThreads * r;
+      const int ci = tid + NT * r;
       kr[r] = buf_load16(rk, (uint32_t)(ci / (D / 8)) * rsb + 16u * (ci % (D / 8)));
     }
 #pragma unroll
     for (int r = 0; r < VPT; ++r) {
-      const int vi = tid + kFwdThreads * r;
+      const int vi = tid + NT * r;
+      if (VU % NT != 0 && vi >= VU) break;
       const uint32_t off = (uint32_t)(2 * (vi % (BK / 2))) * rsb + 16u * (vi / (BK / 2));
       vr[r][0] = buf_load16(rv, off);
       vr[r][1] = buf_load16(rv, off + rsb);
@@ -299,12 +304,13 @@ struct StageBF {
     constexpr int KS = SmemBF<D>::KS, VS = SmemBF<D>::VS;
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
-      const int ci = tid + kFwdThreads * r;
+      const int ci = tid + NT * r;
       *reinterpret_cast<uint4 *>(&kdst[(ci / (D / 8)) * KS + 8 * (ci % (D / 8))]) = kr[r];
     }
 #pragma unroll
     for (int r = 0; r < VPT; ++r) {
-      const int vi = tid + kFwdThreads * r;
+      const int vi = tid + NT * r;
+      if (VU % NT != 0 && vi >= VU) break;
       const int kp = vi % (BK / 2), c8 = vi / (BK / 2);
       const int pos = perm16(2 * kp);  // even; key 2kp+1 lands at pos + 1
       const uint32_t a[4] = {vr[r][0].x, vr[r][0].y, vr[r][0].z, vr[r][0].w};
@@ -353,8 +359,9 @@ __device__ __forceinline__ void scores_again(const __bf16 *ks, const bf16x8 (&qf
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(
+// NW waves (32 query slots each) per work item.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
     const WorkItem *__restrict__ items, const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const __bf16 *__restrict__ V, __bf16 *__restrict__ O, float *__restrict__ LSE, int Hs,
     int64_t Ns, float scale, float scale_log2, int causal, int window) {
@@ -392,7 +399,8 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(
   bool first = true;    // no active tile seen yet (wave-uniform)
 
   const int nk = (it.k1 - it.k0 + BK - 1) / BK;
-  StageBF<D> st;
+  constexpr int NT = 64 * NW;
+  StageBF<D, NT> st;
   st.load(Kh + (int64_t)it.k0 * rs, Vh + (int64_t)it.k0 * rs, it.k1 - it.k0, rsb, tid);
   st.store(sm.k[0], sm.vt[0], tid);
   if (nk > 1)
@@ -418,12 +426,12 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(
         for (int c = 0; c < D / 16; ++c)
           a[beta][c] =
               *reinterpret_cast<const bf16x8 *>(&ks[(32 * beta + l32) * KS + 16 * c + 8 * h]);
+      // key half 0 first: its weights can start while half 1 is multiplied
       floatx16 s[2] = {floatx16{}, floatx16{}};
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        s[0] = mfma32x32x16(a[0][c], qf[c], s[0]);
-        s[1] = mfma32x32x16(a[1][c], qf[c], s[1]);
-      }
+      for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) s[beta] = mfma32x32x16(a[beta][c], qf[c], s[beta]);
       if (!full) mask_tile(s, kt0, it.k1, qi, h, causal, window);
       // weights against the current reference max; the row max is only taken
       // on the wave's first tile and when some weight would exceed 2^64 (a
@@ -481,11 +489,11 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
           for (int e = 0; e < 8; ++e) pf[beta][mm][e] = (__bf16)s[beta][8 * mm + e];
 #pragma unroll
-      for (int dl = 0; dl < D / 32; ++dl)
+      for (int beta = 0; beta < 2; ++beta)
 #pragma unroll
-        for (int beta = 0; beta < 2; ++beta)
+        for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-          for (int mm = 0; mm < 2; ++mm) {
+          for (int dl = 0; dl < D / 32; ++dl) {
             const bf16x8 va = *reinterpret_cast<const bf16x8 *>(
                 &vts[(32 * dl + l32) * VS + 32 * beta + 16 * mm + 8 * h]);
             o[dl] = mfma32x32x16(va, pf[beta][mm], o[dl]);
@@ -526,13 +534,19 @@ hipError_t launch_typed(const attn_plan *p, const void *q, const void *k, const 
   if (n == 0) return hipSuccess;
   const float scale = p->p.scale;
   const float scale_log2 = scale * 1.4426950408889634f;
-  if (std::is_same<T, __bf16>::value)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3(n), dim3(kFwdThreads), 0, stream, items,
-                       static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
+  if (std::is_same<T, __bf16>::value && p->fwd_bq == kFwdBQ)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, kFwdBQ / 32>), dim3(n), dim3(2 * kFwdBQ), 0, stream,
+                       items, static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
                        static_cast<const __bf16 *>(v), static_cast<__bf16 *>(o), lse, p->p.Hs,
                        p->p.Ns, scale, scale_log2, p->p.causal, p->p.window);
+  else if (std::is_same<T, __bf16>::value)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, kFwdBQShort / 32>), dim3(n), dim3(2 * kFwdBQShort), 0,
+                       stream, items, static_cast<const __bf16 *>(q),
+                       static_cast<const __bf16 *>(k), static_cast<const __bf16 *>(v),
+                       static_cast<__bf16 *>(o), lse, p->p.Hs, p->p.Ns, scale, scale_log2,
+                       p->p.causal, p->p.window);
   else
-    hipLaunchKernelGGL((fwd_kernel<float, D>), dim3(n), dim3(kFwdThreads), 0, stream, items,
+    hipLaunchKernelGGL((fwd_kernel<float, D>), dim3(n), dim3(kFwdThreadsF32), 0, stream, items,
                        static_cast<const float *>(q), static_cast<const float *>(k),
                        static_cast<const float *>(v), static_cast<float *>(o), lse, p->p.Hs,
                        p->p.Ns, scale, scale_log2, p->p.causal, p->p.window);

@@ -12,11 +12,21 @@ namespace attn {
 
 // Tile shapes.  The host plan cuts work items with these, the kernels assume
 // them; both sides include this header.
-//   forward (and the dQ pass of the backward): BQ query slots per work item,
-//   BK key slots per inner step.  Four waves, 32 queries per wave.
-constexpr int kFwdBQ = 128;
+//   forward: BQ query slots per work item, BK key slots per inner step, 32
+//   queries per wave.  bf16 runs eight waves per item (each staged K/V tile
+//   serves 256 queries) unless the window is short, where a 256-query item
+//   would stage mostly keys that most of its waves skip: then four.  fp32 runs
+//   four, its registers do not allow more.
+constexpr int kFwdBQ = 256;
+constexpr int kFwdBQShort = 128;
+constexpr int kFwdShortWindow = 512;  // windows up to this use kFwdBQShort
+constexpr int kFwdBQF32 = 128;
+constexpr int kFwdThreadsF32 = 256;
 constexpr int kFwdBK = 64;
-constexpr int kFwdThreads = 256;
+//   backward dQ pass: 128 query slots per item, four waves, BK key slots per
+//   step.
+constexpr int kDqBQ = 128;
+constexpr int kDqThreads = 256;
 //   backward dK/dV pass: BKB key slots per work item, BQB query slots per step.
 constexpr int kBwdBK = 128;
 constexpr int kBwdBQ = 64;
@@ -26,7 +36,7 @@ constexpr int kRopeThreads = 256;
 // Work-list chunk: consecutive tiles of one head and sequence kept on one XCD.
 constexpr int kXcdChunk = 16;
 
-// One work item of the forward / dQ pass: attention head `head`, query slots
+// One work item of the forward or dQ pass: attention head `head`, query slots
 // [q0, q1) inside one sequence, key slots [k0, k1) that any of those queries
 // may see.  For the dK/dV pass the roles swap: keys [q0, q1) of the item,
 // queries [k0, k1) that may see them.
@@ -60,12 +70,15 @@ struct attn_plan {
   std::vector<float> rope_cos;      // [P, d/2]
   std::vector<float> rope_sin;      // [P, d/2]
   int32_t max_pos = 0;              // P
-  std::vector<attn::WorkItem> fwd;  // forward / dQ items, longest first
-  std::vector<attn::WorkItem> bwd;  // dK/dV items, longest first
+  int32_t fwd_bq = 0;               // query slots per forward item
+  std::vector<attn::WorkItem> fwd;  // forward items
+  std::vector<attn::WorkItem> bwd;  // dK/dV items
+  std::vector<attn::WorkItem> dq;   // dQ items (bf16 problems only)
   attn_plan_info info{};
 
   // Workspace layout (byte offsets; every section 256-byte aligned).
-  size_t off_pos = 0, off_cos = 0, off_sin = 0, off_fwd = 0, off_bwd = 0, off_delta = 0;
+  size_t off_pos = 0, off_cos = 0, off_sin = 0, off_fwd = 0, off_bwd = 0, off_dq = 0;
+  size_t off_delta = 0;
   size_t ws_bytes = 0;
   // Bound workspace.
   char *ws = nullptr;

@@ -214,17 +214,25 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
     // Work lists and exact counts.
     int64_t pairs = 0;
     int stream = 0;
+    const bool bf16 = P.dtype == ATTN_BF16;  // the backward is bf16 only
+    p->fwd_bq = !bf16 ? attn::kFwdBQF32
+                : (P.window > 0 && P.window <= attn::kFwdShortWindow) ? attn::kFwdBQShort
+                                                                      : attn::kFwdBQ;
     for (int j = 0; j < P.Hs; ++j)
       for (int s = 0; s < S; ++s) {
         const int64_t b = (int64_t)cu[s] * mult, e = (int64_t)cu[s + 1] * mult;
         if (e == b) continue;
         pairs += visible_pairs_of(e - b, P.causal, P.window);
-        cut_items(p->fwd, j, stream, b, e, attn::kFwdBQ, P.causal, P.window, true);
-        cut_items(p->bwd, j, stream, b, e, attn::kBwdBK, P.causal, P.window, false);
+        cut_items(p->fwd, j, stream, b, e, p->fwd_bq, P.causal, P.window, true);
+        if (bf16) {
+          cut_items(p->bwd, j, stream, b, e, attn::kBwdBK, P.causal, P.window, false);
+          cut_items(p->dq, j, stream, b, e, attn::kDqBQ, P.causal, P.window, true);
+        }
         ++stream;
       }
     order_for_xcds(p->fwd, attn::kFwdBK, attn::kXcdChunk);
     order_for_xcds(p->bwd, attn::kBwdBQ, attn::kXcdChunk);
+    order_for_xcds(p->dq, attn::kFwdBK, attn::kXcdChunk);
 
     const double elems = (double)P.N * P.H * P.d;
     const double es = P.dtype == ATTN_BF16 ? 2.0 : 4.0;
@@ -254,6 +262,8 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
     off = align256(off + sizeof(WorkItem) * p->fwd.size());
     p->off_bwd = off;
     off = align256(off + sizeof(WorkItem) * p->bwd.size());
+    p->off_dq = off;
+    off = align256(off + sizeof(WorkItem) * p->dq.size());
     p->off_delta = off;
     off = align256(off + sizeof(float) * (size_t)P.Ns * P.Hs);
     p->ws_bytes = std::max<size_t>(off, 256);
@@ -283,6 +293,7 @@ attn_status attn_plan_bind(attn_plan *p, void *ws, size_t bytes, void *stream) {
       {p->off_sin, p->rope_sin.data(), sizeof(float) * p->rope_sin.size()},
       {p->off_fwd, p->fwd.data(), sizeof(WorkItem) * p->fwd.size()},
       {p->off_bwd, p->bwd.data(), sizeof(WorkItem) * p->bwd.size()},
+      {p->off_dq, p->dq.data(), sizeof(WorkItem) * p->dq.size()},
   };
   for (const Sec &s : secs) {
     if (s.n == 0) continue;
@@ -301,8 +312,8 @@ attn_status attn_plan_stats(const attn_plan *p, attn_plan_info *info) {
 
 attn_status attn_plan_work_items(const attn_plan *p, int32_t which, int32_t *out,
                                  int64_t capacity, int64_t *count) {
-  if (!p || !count || (which != 0 && which != 1) || capacity < 0) return ATTN_E_INVALID;
-  const std::vector<WorkItem> &v = which == 0 ? p->fwd : p->bwd;
+  if (!p || !count || which < 0 || which > 2 || capacity < 0) return ATTN_E_INVALID;
+  const std::vector<WorkItem> &v = which == 0 ? p->fwd : which == 1 ? p->bwd : p->dq;
   *count = (int64_t)v.size();
   const int64_t n = std::min<int64_t>(capacity, (int64_t)v.size());
   if (n > 0 && !out) return ATTN_E_INVALID;
