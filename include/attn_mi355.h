@@ -133,9 +133,9 @@ attn_status attn_plan_stats(const attn_plan *plan, attn_plan_info *info);
 /*
  * Introspection of the tile work lists (host only), for testing and
  * scheduling analysis.  which = 0: forward items (256 query slots each for
- * bf16, 128 for fp32); which = 1: backward key-tile items (128 key slots);
- * which = 2: backward dQ items (128 query slots).  The backward lists are
- * empty for fp32 problems.
+ * bf16, 128 for fp32 and for windows of at most 512 slots); which = 1:
+ * backward key-tile items (128 key slots); which = 2: backward dQ items (128
+ * query slots).  The backward lists are empty for fp32 problems.
  * Each item is 8 int32: {attention head, r0, r1, s0, s1, stream, 0, 0}
  * where stream numbers the (attention head, sequence) pairs.  The list order
  * is the launch order: item i runs as workgroup i, on XCD i mod 8; items of one

@@ -78,15 +78,17 @@ def test_empty_problem_is_valid():
 
 
 def test_item_sizes_follow_the_dtype():
-    # bf16: 256-query forward items, 128-query dQ items, 128-key dK/dV items;
-    # fp32 (no backward): 128-query forward items and empty backward lists
+    # bf16: 256-query forward items, 128-row backward dK/dV (keys) and dQ
+    # (queries) items; fp32 (no backward): 128-query forward items and empty
+    # backward lists
     cu = [0, 700]
     pb = plan(num_tokens=700, cu_seqlens=cu)
+    pb128 = plan(num_tokens=700, cu_seqlens=cu, head_dim=128)
     pf = plan(num_tokens=700, cu_seqlens=cu, dtype="fp32")
-    assert (np.diff(pb.work_items(0)[:, 1:3], axis=1).max()) == 256
-    assert (np.diff(pb.work_items(2)[:, 1:3], axis=1).max()) == 128
-    assert (np.diff(pb.work_items(1)[:, 1:3], axis=1).max()) == 128
-    assert (np.diff(pf.work_items(0)[:, 1:3], axis=1).max()) == 128
+    rows = lambda p, which: np.diff(p.work_items(which)[:, 1:3], axis=1).max()
+    assert rows(pb, 0) == 256 and rows(pb, 1) == 128 and rows(pb, 2) == 128
+    assert rows(pb128, 0) == 256 and rows(pb128, 1) == 128 and rows(pb128, 2) == 128
+    assert rows(pf, 0) == 128
     # a short window keeps 128-query forward items (a longer one does not)
     assert np.diff(plan(num_tokens=700, cu_seqlens=cu, window=512).work_items(0)[:, 1:3],
                    axis=1).max() == 128

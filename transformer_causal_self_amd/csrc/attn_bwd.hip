@@ -70,10 +70,10 @@ __device__ __forceinline__ uint32_t pair_word(const uint4 &a, const uint4 &b, in
 // zero): `nat` gets the rows as they are (row stride D + 8), `tr` (optional)
 // the transpose with rows permuted by perm16 (row stride 72).  Work unit of a
 // thread: a pair of rows x 8 features.
-template <int D>
+template <int D, int NT>
 struct PairStage {
   static constexpr int UNITS = 32 * (D / 8);
-  static constexpr int PT = UNITS / 256;  // units per thread
+  static constexpr int PT = (UNITS + NT - 1) / NT;  // units per thread (NT threads)
   uint4 r[PT][2];
   // rows [t0, t0 + 64) of the head whose first slot is `base`; rows at or past
   // `lim` read zero (the buffer resource ends there)
@@ -82,7 +82,8 @@ struct PairStage {
     const auto rsrc = make_rsrc(base + (int64_t)t0 * rs, (uint32_t)max(0, min(lim - t0, 64)) * rsb);
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
-      const int id = tid + 256 * u;
+      const int id = tid + NT * u;
+      if (UNITS % NT != 0 && id >= UNITS) break;
       const int rp = id % 32, c8 = id / 32;
 #pragma unroll
       for (int e = 0; e < 2; ++e)
@@ -93,7 +94,8 @@ struct PairStage {
     constexpr int RS = D + 8, TS = 72;
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
-      const int id = tid + 256 * u;
+      const int id = tid + NT * u;
+      if (UNITS % NT != 0 && id >= UNITS) break;
       const int rp = id % 32, c8 = id / 32;
       *reinterpret_cast<uint4 *>(&nat[(2 * rp) * RS + 8 * c8]) = r[u][0];
       *reinterpret_cast<uint4 *>(&nat[(2 * rp + 1) * RS + 8 * c8]) = r[u][1];
@@ -141,8 +143,8 @@ struct DkvSmem {
   DkvBuf<D> b[2];  // double buffered: one barrier per query tile
 };
 
-template <int D>
-__global__ __launch_bounds__(kBwdThreads, bwd_min_blocks<D>()) void dkv_kernel(
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dkv_kernel(
     const WorkItem *__restrict__ items, const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const __bf16 *__restrict__ V, const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
     const float *__restrict__ delta, float *__restrict__ dK, float *__restrict__ dV, int Hs,
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_blocks<D>()) void dkv_kernel(
   for (int dl = 0; dl < D / 32; ++dl) dv[dl] = dk[dl] = floatx16{};
 
   const int nq = (it.k1 - it.k0 + BQ - 1) / BQ;
-  PairStage<D> sq, sg;
+  PairStage<D, 64 * NW> sq, sg;
   float st_lse = 0.0f;
   auto load_tile = [&](int q0) {
     sq.load(Q + ho, rs, q0, it.k1, tid);
@@ -211,12 +213,14 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_blocks<D>()) void dkv_kernel(
     const int qhi = min(it.k1 - 1, window > 0 ? kj + window - 1 : (1 << 30)) - qt0;
 #pragma unroll
     for (int rho = 0; rho < BQ / 32; ++rho) {
+      // S first: its exponentials can start while dP is multiplied
       floatx16 s = {}, dp = {};
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
+      for (int c = 0; c < D / 16; ++c)
         s = mfma32x32x16(load_bf16x8(&cur.q[(32 * rho + l32) * RS + 16 * c + 8 * h]), kf[c], s);
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
         dp = mfma32x32x16(load_bf16x8(&cur.g[(32 * rho + l32) * RS + 16 * c + 8 * h]), vf[c], dp);
-      }
       // rows of s: query 32*rho + 8b + 4h + i of the tile; column: key kj
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
@@ -281,8 +285,8 @@ struct DqSmem {
   DqBuf<D> b[2];  // double buffered: one barrier per key tile
 };
 
-template <int D>
-__global__ __launch_bounds__(kDqThreads, bwd_min_blocks<D>()) void dq_kernel(
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dq_kernel(
     const WorkItem *__restrict__ items, const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const __bf16 *__restrict__ V, const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
     const float *__restrict__ delta, float *__restrict__ dQ, int Hs, int64_t Ns, float scale,
@@ -316,7 +320,7 @@ __global__ __launch_bounds__(kDqThreads, bwd_min_blocks<D>()) void dq_kernel(
   for (int dl = 0; dl < D / 32; ++dl) dq[dl] = floatx16{};
 
   const int nk = (it.k1 - it.k0 + BK - 1) / BK;
-  PairStage<D> sk, sv;
+  PairStage<D, 64 * NW> sk, sv;
   sk.load(K + ho, rs, it.k0, it.k1, tid);
   sv.load(V + ho, rs, it.k0, it.k1, tid);
   sk.store(sm.b[0].k, sm.b[0].kt, tid);
@@ -344,11 +348,13 @@ __global__ __launch_bounds__(kDqThreads, bwd_min_blocks<D>()) void dq_kernel(
     for (int beta = 0; beta < 2; ++beta) {
       s[beta] = dp[beta] = floatx16{};
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const int off = (32 * beta + l32) * RS + 16 * c + 8 * h;
-        s[beta] = mfma32x32x16(load_bf16x8(&cur.k[off]), qf[c], s[beta]);
-        dp[beta] = mfma32x32x16(load_bf16x8(&cur.v[off]), gf[c], dp[beta]);
-      }
+      for (int c = 0; c < D / 16; ++c)
+        s[beta] = mfma32x32x16(load_bf16x8(&cur.k[(32 * beta + l32) * RS + 16 * c + 8 * h]), qf[c],
+                               s[beta]);
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+        dp[beta] = mfma32x32x16(load_bf16x8(&cur.v[(32 * beta + l32) * RS + 16 * c + 8 * h]),
+                                gf[c], dp[beta]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(fmaf(s[beta][r], scale_log2, -lse2));
@@ -401,14 +407,15 @@ hipError_t launch_typed(const attn_plan *p, const void *q, const void *k, const 
   const __bf16 *V = static_cast<const __bf16 *>(v), *O = static_cast<const __bf16 *>(o);
   const __bf16 *G = static_cast<const __bf16 *>(d_o);
   const int64_t rows = Ns * Hs;
+  constexpr int NWK = kBwdWaves, NWQ = kBwdWaves;
   hipLaunchKernelGGL((delta_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
                      O, G, delta, Hs, Ns);
   if (!p->bwd.empty())
-    hipLaunchKernelGGL((dkv_kernel<D>), dim3((unsigned)p->bwd.size()), dim3(kBwdThreads), 0,
+    hipLaunchKernelGGL((dkv_kernel<D, NWK>), dim3((unsigned)p->bwd.size()), dim3(64 * NWK), 0,
                        stream, reinterpret_cast<const WorkItem *>(p->ws + p->off_bwd), Q, K, V, G,
                        lse, delta, dk, dv, Hs, Ns, scale, scale_log2, p->p.causal, p->p.window);
   if (!p->dq.empty())
-    hipLaunchKernelGGL((dq_kernel<D>), dim3((unsigned)p->dq.size()), dim3(kDqThreads), 0,
+    hipLaunchKernelGGL((dq_kernel<D, NWQ>), dim3((unsigned)p->dq.size()), dim3(64 * NWQ), 0,
                        stream, reinterpret_cast<const WorkItem *>(p->ws + p->off_dq), Q, K, V, G,
                        lse, delta, dq, Hs, Ns, scale, scale_log2, p->p.causal, p->p.window);
   return hipGetLastError();

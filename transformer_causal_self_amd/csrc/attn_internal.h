@@ -23,14 +23,13 @@ constexpr int kFwdShortWindow = 512;  // windows up to this use kFwdBQShort
 constexpr int kFwdBQF32 = 128;
 constexpr int kFwdThreadsF32 = 256;
 constexpr int kFwdBK = 64;
-//   backward dQ pass: 128 query slots per item, four waves, BK key slots per
-//   step.
-constexpr int kDqBQ = 128;
-constexpr int kDqThreads = 256;
-//   backward dK/dV pass: BKB key slots per work item, BQB query slots per step.
-constexpr int kBwdBK = 128;
+//   backward: both passes run four waves of 32 rows (keys for dK/dV, queries
+//   for dQ) per work item and step over 64 partner rows at a time.  (Eight
+//   waves per item, which halves the staging per row, measured slower here:
+//   one block per CU instead of two.)
+constexpr int kBwdWaves = 4;
+constexpr int kBwdRows = 32 * kBwdWaves;
 constexpr int kBwdBQ = 64;
-constexpr int kBwdThreads = 256;
 //   rotary: threads per block.
 constexpr int kRopeThreads = 256;
 // Work-list chunk: consecutive tiles of one head and sequence kept on one XCD.

@@ -225,8 +225,8 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
         pairs += visible_pairs_of(e - b, P.causal, P.window);
         cut_items(p->fwd, j, stream, b, e, p->fwd_bq, P.causal, P.window, true);
         if (bf16) {
-          cut_items(p->bwd, j, stream, b, e, attn::kBwdBK, P.causal, P.window, false);
-          cut_items(p->dq, j, stream, b, e, attn::kDqBQ, P.causal, P.window, true);
+          cut_items(p->bwd, j, stream, b, e, attn::kBwdRows, P.causal, P.window, false);
+          cut_items(p->dq, j, stream, b, e, attn::kBwdRows, P.causal, P.window, true);
         }
         ++stream;
       }
