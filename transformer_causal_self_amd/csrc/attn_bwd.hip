@@ -152,7 +152,8 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dkv_kernel(
   constexpr int RS = DkvSmem<D>::RS, TS = DkvSmem<D>::TS, BQ = kBwdBQ;
   __shared__ __attribute__((aligned(16))) DkvSmem<D> sm;
   const WorkItem it = items[blockIdx.x];  // keys [q0, q1), queries [k0, k1)
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int h = lane >> 5, l32 = lane & 31;
   const int64_t rs = (int64_t)Hs * D;
   const int64_t ho = (int64_t)it.head * D;
@@ -294,7 +295,8 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dq_kernel(
   constexpr int RS = DqSmem<D>::RS, TS = DqSmem<D>::TS, BK = kFwdBK;
   __shared__ __attribute__((aligned(16))) DqSmem<D> sm;
   const WorkItem it = items[blockIdx.x];  // queries [q0, q1), keys [k0, k1)
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int h = lane >> 5, l32 = lane & 31;
   const int64_t rs = (int64_t)Hs * D;
   const int64_t ho = (int64_t)it.head * D;

@@ -156,7 +156,8 @@ __global__ __launch_bounds__(kFwdThreadsF32, fwd_min_blocks<T>()) void fwd_kerne
     float scale, float scale_log2, int causal, int window) {
   __shared__ __attribute__((aligned(16))) Smem<T, D> sm;
   const WorkItem it = items[blockIdx.x];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int h = lane >> 5, l32 = lane & 31;
   const int64_t rs = (int64_t)Hs * D;  // elements between consecutive slots
   const T *Qh = Q + (int64_t)it.head * D;
@@ -368,7 +369,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
   constexpr int KS = SmemBF<D>::KS, VS = SmemBF<D>::VS;
   __shared__ __attribute__((aligned(16))) SmemBF<D> sm;
   const WorkItem it = items[blockIdx.x];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int h = lane >> 5, l32 = lane & 31;
   const int64_t rs = (int64_t)Hs * D;  // elements between consecutive slots
   const uint32_t rsb = (uint32_t)rs * 2u;
