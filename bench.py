@@ -1,6 +1,7 @@
 """Benchmark of the rotary causal self-attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--paired P]
+                    [--no-cpu-baseline]
 
 One step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: rope_qkv (Q, K rotated), attn_fwd (O, LSE) and, for
@@ -40,6 +41,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--paired", type=int, choices=(0, 1, 2), default=None,
+                    help="override the workload's head pairing (2: adjacent partner h^1, "
+                         "where rope_qkv also copies V in the slot layout)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -135,6 +139,10 @@ def main():
     from transformer_causal_self_amd import workloads as wl
 
     w = wl.WORKLOADS[args.workload]
+    if args.paired is not None:
+        import dataclasses
+        w = dataclasses.replace(w, paired=args.paired)
+    copy_v = w.paired == 2      # V' must be written in the slot layout
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = wl.generate(w)
@@ -146,15 +154,22 @@ def main():
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
     do = inp["do"].to(dev) if w.backward else None
     q2, k2 = torch.empty_like(q), torch.empty_like(k)
+    v2 = torch.empty_like(v) if copy_v else v
     o = torch.empty_like(q)
     lse = torch.empty((info["attn_heads"], info["slots"]), dtype=torch.float32, device=dev)
     grads = None
-    tca.rope_qkv(plan, q, k, q_out=q2, k_out=k2)
-    tca.attn_fwd(plan, q2, k2, v, o, lse)
+    def rope():
+        if copy_v:
+            tca.rope_qkv(plan, q, k, v, q_out=q2, k_out=k2, v_out=v2)
+        else:
+            tca.rope_qkv(plan, q, k, q_out=q2, k_out=k2)
+
+    rope()
+    tca.attn_fwd(plan, q2, k2, v2, o, lse)
     if w.backward:
         grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
         try:
-            tca.attn_bwd(plan, q2, k2, v, o, lse, do, *grads)
+            tca.attn_bwd(plan, q2, k2, v2, o, lse, do, *grads)
         except tca.AttnError as e:
             if e.status != -2:
                 raise
@@ -174,10 +189,10 @@ def main():
                 events[name].append((a, b))
             else:
                 fn()
-        timed("rope_qkv", lambda: tca.rope_qkv(plan, q, k, q_out=q2, k_out=k2))
-        timed("attn_fwd", lambda: tca.attn_fwd(plan, q2, k2, v, o, lse))
+        timed("rope_qkv", rope)
+        timed("attn_fwd", lambda: tca.attn_fwd(plan, q2, k2, v2, o, lse))
         if grads is not None:
-            timed("attn_bwd", lambda: tca.attn_bwd(plan, q2, k2, v, o, lse, do, *grads))
+            timed("attn_bwd", lambda: tca.attn_bwd(plan, q2, k2, v2, o, lse, do, *grads))
 
     for _ in range(args.warmup):
         step(False)
@@ -198,14 +213,16 @@ def main():
 
     kern_ms = {n: sum(a.elapsed_time(b) for a, b in events[n]) / len(events[n]) for n in names}
     digest = kernel_sources_digest()
-    wname = f"problem{w.num}"
+    wname = f"problem{w.num}" + ("" if args.paired is None else f"-paired{w.paired}")
+    # rope_qkv algorithmic bytes: Q, K read and written (plus V when copied)
+    rope_bytes = info["rope_bytes"] * (1.5 if copy_v else 1.0)
     step_flops = info["fwd_flops"] + (info["bwd_flops"] if grads is not None else 0.0)
     kernels = {}
     peak_mm = PEAK_BF16_TFLOPS if w.dtype == wl.DTYPE_BF16 else PEAK_FP32_TFLOPS
     for n in names:
         t = kern_ms[n] * 1e-3
         if n == "rope_qkv":
-            ach = info["rope_bytes"] / t / 1e9
+            ach = rope_bytes / t / 1e9
             rl = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                   "frac": ach / PEAK_HBM_GBS}
         else:
@@ -235,7 +252,7 @@ def main():
         "data": "synthetic (seeded N(0,1) Q, K, V, dO; fixed sequence layout)",
         "config": {"workload": w.name, "tokens": w.n_tokens, "heads": w.heads,
                    "head_dim": w.head_dim, "sequences": len(inp["cu"]) - 1,
-                   "window": w.window, "paired": w.paired,
+                   "window": w.window, "paired": w.paired, "v_copied_by_rope": copy_v,
                    "rope": {1: "half-split", 2: "adjacent"}.get(w.rope, "none"),
                    "step": "+".join(names), "parallelism": "single GPU"},
         "roofline": roof,

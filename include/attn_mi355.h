@@ -15,6 +15,8 @@
  *      sections "Core idea" and "Source 4: Triton kernel interleave indexing"
  *        -- head h of token t becomes slot 2t + h / (H/2) of attention head
  *        h mod (H/2): the sequence doubles and the head count halves;
+ *      section "Core idea" -- the K/Q/V of two adjacent heads are interleaved
+ *        per position (the ATTN_PAIRED_ADJACENT reading: partner h ^ 1);
  *      section "Sequence length and window" -- sequence boundaries double,
  *        the window (in key slots) does not;
  *      sections "Zero-copy RoPE", "Staggered rotary", "Source 2: paired
@@ -29,8 +31,14 @@
  *
  * Layouts (row-major, element strides):
  *   Q, K, V, O         [N, H, d]  token-major, each token's H*d values contiguous.
- *                      When paired the same memory is read as [2N, H/2, d]:
- *                      slot 2t + h / (H/2), attention head h mod (H/2).
+ *                      When paired (ATTN_PAIRED) the same memory is read as
+ *                      [2N, H/2, d]: slot 2t + h / (H/2), attention head
+ *                      h mod (H/2).  With ATTN_PAIRED_ADJACENT, head h goes to
+ *                      slot 2t + (h mod 2), attention head h / 2; the [2N, H/2, d]
+ *                      buffers (Q', K', V' from rope_qkv, O, dQ, dK, dV) then
+ *                      hold token t's heads in the order 0, 2, 4, ..., 1, 3, 5,
+ *                      ...: head h at position (h mod 2) * H/2 + h / 2 of the
+ *                      token's H*d row.
  *   LSE                float [H', N'] (attention head, slot); natural log.
  *   dQ, dK, dV         float [N, H, d] (same slot view as Q when paired).
  *   N' = 2N, H' = H/2 when paired; else N' = N, H' = H.
@@ -72,7 +80,7 @@ typedef enum {
 
 enum { ATTN_BF16 = 0, ATTN_FP32 = 1 };
 enum { ATTN_ROPE_NONE = 0, ATTN_ROPE_HALF = 1, ATTN_ROPE_ADJACENT = 2 };
-enum { ATTN_UNPAIRED = 0, ATTN_PAIRED = 1 };
+enum { ATTN_UNPAIRED = 0, ATTN_PAIRED = 1, ATTN_PAIRED_ADJACENT = 2 };
 
 typedef struct {
   int64_t num_tokens;        /* N >= 0 */
@@ -87,7 +95,8 @@ typedef struct {
   float softmax_scale;       /* s; 0 selects 1/sqrt(head_dim) */
   int32_t rope;              /* ATTN_ROPE_NONE, _HALF (pairs i, i+d/2), _ADJACENT (2i, 2i+1) */
   double rope_base;          /* frequencies base^(-2i/d); e.g. 10000 */
-  int32_t paired;            /* ATTN_UNPAIRED or ATTN_PAIRED */
+  int32_t paired;            /* ATTN_UNPAIRED, ATTN_PAIRED (partner h + H/2, the
+                                memory view) or ATTN_PAIRED_ADJACENT (partner h ^ 1) */
 } attn_problem;
 
 /* Counts for throughput and roofline reporting (exact, from the plan). */
@@ -160,6 +169,9 @@ attn_status attn_plan_work_items(const attn_plan *plan, int32_t which, int32_t *
  * for k.  Written dense, the outputs already are the paired interleaved layout.
  * v / v_out: when v_out is not NULL, V (token stride v_tok_stride) is copied
  * dense into v_out in the same pass; when v_out is NULL, v is ignored.
+ * ATTN_PAIRED_ADJACENT: the outputs are written in that layout's head order
+ * (see Layouts), so v_out is required (V' feeds attn_fwd) and neither output
+ * may alias its input (ATTN_E_INVALID otherwise).
  * The plan's rope mode must not be ATTN_ROPE_NONE (ATTN_E_INVALID).
  */
 attn_status rope_qkv(const attn_plan *plan, const void *q, int64_t q_tok_stride, const void *k,

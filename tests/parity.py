@@ -69,7 +69,31 @@ def slot_to_token(s, j, H, paired):
     """Inverse of the paired slot map: (slot, attention head) -> (token, head)."""
     if not paired:
         return s, j
+    if paired == 2:
+        return s // 2, 2 * j + s % 2
     return s // 2, j + (s % 2) * (H // 2)
+
+
+def adjacent_order(H):
+    """Position of head h inside a token's row in the adjacent-pairing layout
+    (slot 2t + h mod 2, attention head h // 2, read as [2N, H/2, d])."""
+    return np.array([(h % 2) * (H // 2) + h // 2 for h in range(H)])
+
+
+def to_slot_layout(x, H, paired):
+    """[N, H, d] in head order -> the library's slot-layout memory."""
+    if paired != 2:
+        return x
+    y = torch.empty_like(x)
+    y[:, torch.from_numpy(adjacent_order(H))] = x
+    return y
+
+
+def from_slot_layout(x, H, paired):
+    """Inverse of to_slot_layout (numpy or torch, [N, H, d])."""
+    if paired != 2:
+        return x
+    return x[:, adjacent_order(H)]
 
 
 def sample_rows(w, cu, rng, n_random=48):

@@ -60,7 +60,8 @@ def plan(**kw):
     (dict(rope_base=0.0), -1),
     (dict(softmax_scale=float("nan")), -1),
     (dict(softmax_scale=-1.0), -1),
-    (dict(paired=2, num_heads=4), -1),
+    (dict(paired=3, num_heads=4), -1),
+    (dict(paired=2, num_heads=3), -1),                 # odd heads, adjacent pairing
     (dict(head_dim=32), -2),                           # valid, not covered by the kernels
     (dict(head_dim=96), -2),
 ])
@@ -113,6 +114,7 @@ CASES = [
     ([0, 50, 300], 2, 0, 1, 1),
     ([0, 129, 300], 4, 1, 1, 129),
     ([0, 90, 300], 2, 0, 0, 0),
+    ([0, 130, 400], 6, 2, 1, 128),                      # adjacent pairing: same slots
 ]
 
 

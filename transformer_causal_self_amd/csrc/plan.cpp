@@ -152,7 +152,9 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
   if (pr->rope < ATTN_ROPE_NONE || pr->rope > ATTN_ROPE_ADJACENT) return ATTN_E_INVALID;
   if (pr->rope != ATTN_ROPE_NONE && !(pr->rope_base > 0.0 && std::isfinite(pr->rope_base)))
     return ATTN_E_INVALID;
-  if (pr->paired != ATTN_UNPAIRED && pr->paired != ATTN_PAIRED) return ATTN_E_INVALID;
+  if (pr->paired != ATTN_UNPAIRED && pr->paired != ATTN_PAIRED &&
+      pr->paired != ATTN_PAIRED_ADJACENT)
+    return ATTN_E_INVALID;
   if (pr->paired && (pr->num_heads % 2)) return ATTN_E_INVALID;
   if (!std::isfinite(pr->softmax_scale) || pr->softmax_scale < 0.0f) return ATTN_E_INVALID;
   if (pr->head_dim <= 0 || (pr->head_dim % 2)) return ATTN_E_INVALID;
@@ -339,6 +341,10 @@ attn_status rope_qkv(const attn_plan *p, const void *q, int64_t qs, const void *
       (v_out && (!aligned16(v) || !aligned16(v_out))))
     return ATTN_E_ALIGN;
   if ((q_out == q && qs != row) || (k_out == k && ks != row)) return ATTN_E_INVALID;
+  // the adjacent pairing permutes heads on store: V must be copied with them,
+  // and an in-place store would overwrite heads not yet read
+  if (p->p.paired == ATTN_PAIRED_ADJACENT && (!v_out || q_out == q || k_out == k))
+    return ATTN_E_INVALID;
   return attn::launch_rope(p, q, qs, k, ks, v_out ? v : nullptr, vs, q_out, k_out, v_out,
                            static_cast<hipStream_t>(stream));
 }

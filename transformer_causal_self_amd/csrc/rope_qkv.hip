@@ -15,6 +15,11 @@
 // Work split: one thread owns one token and two 16-byte units of every head
 // row, and walks the H heads, so its cos/sin values (fp32, read from the table,
 // L2 resident) are loaded once per token and reused for every head of Q and K.
+//
+// The adjacent pairing (partner h ^ 1; "Paired Head Attention", section "Core
+// idea") puts head h at slot 2t + (h mod 2), attention head h / 2, which in the
+// dense [2N, H/2, d] output is position (h mod 2) * H/2 + h / 2 of the token's
+// row: the store permutes heads (V is copied with the same permutation).
 #include "attn_internal.h"
 #include "device_common.h"
 #include "launch.h"
@@ -108,7 +113,9 @@ struct RopeChunk {
   }
 };
 
-template <typename T, int D, bool HALF, bool PAIRED>
+// PM: 0 unpaired, 1 paired (partner h + H/2, no permutation), 2 paired
+// adjacent (partner h ^ 1, heads permuted on store).
+template <typename T, int D, bool HALF, int PM>
 __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
     const T *q, int64_t qs, const T *k, int64_t ks, const T *__restrict__ v, int64_t vs, T *qo,
     T *ko, T *__restrict__ vo, const int32_t *__restrict__ tok_pos,
@@ -122,8 +129,8 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
   const int t = tok_pos[n];
   float cs[2][NP], sn[2][NP];
 #pragma unroll
-  for (int par = 0; par < (PAIRED ? 2 : 1); ++par) {
-    const int64_t pos = PAIRED ? 2 * t + par : t;
+  for (int par = 0; par < (PM ? 2 : 1); ++par) {
+    const int64_t pos = PM ? 2 * t + par : t;
     const float *cr = tcos + pos * (D / 2), *sr = tsin + pos * (D / 2);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
@@ -136,6 +143,8 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
   const uint4 *k4 = reinterpret_cast<const uint4 *>(k + n * ks);
   uint4 *qo4 = reinterpret_cast<uint4 *>(qo + n * row);
   uint4 *ko4 = reinterpret_cast<uint4 *>(ko + n * row);
+  // output position of head hh inside the token's row
+  auto out_head = [H](int hh) { return PM == 2 ? (hh & 1) * (H / 2) + hh / 2 : hh; };
   int h = 0;
   // two heads per step: eight 16-byte loads in flight before any store
   for (; h + 1 < H; h += 2) {
@@ -150,8 +159,8 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int par = PAIRED ? ((h + e) & 1) : 0;
-      const int base = (h + e) * U;
+      const int par = PM ? ((h + e) & 1) : 0;
+      const int base = out_head(h + e) * U;
       uint4 r0, r1;
       RC::rotate(in[e][0][0], in[e][0][1], cs[par], sn[par], r0, r1);
       qo4[base + c] = r0;
@@ -161,8 +170,8 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
       ko4[base + c + U / 2] = r1;
     }
   }
-  if (h < H) {
-    const int par = PAIRED ? (h & 1) : 0;
+  if (h < H) {  // odd H: unpaired only
+    const int par = PM ? (h & 1) : 0;
     const int base = h * U;
     const uint4 a0 = q4[base + c], a1 = q4[base + c + U / 2];
     const uint4 b0 = k4[base + c], b1 = k4[base + c + U / 2];
@@ -178,8 +187,9 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
     const uint4 *v4 = reinterpret_cast<const uint4 *>(v + n * vs);
     uint4 *vo4 = reinterpret_cast<uint4 *>(vo + n * row);
     for (int hh = 0; hh < H; ++hh) {
-      vo4[hh * U + c] = v4[hh * U + c];
-      vo4[hh * U + c + U / 2] = v4[hh * U + c + U / 2];
+      const int ob = out_head(hh) * U;
+      vo4[ob + c] = v4[hh * U + c];
+      vo4[ob + c + U / 2] = v4[hh * U + c + U / 2];
     }
   }
 }
@@ -202,19 +212,20 @@ hipError_t launch_typed(const attn_plan *p, const void *q, int64_t qs, const voi
   T *KO = static_cast<T *>(ko);
   T *VO = static_cast<T *>(vo);
   const bool half = p->p.rope == ATTN_ROPE_HALF;
-  const bool paired = p->p.paired != 0;
-  if (half && paired)
-    hipLaunchKernelGGL((rope_kernel<T, D, true, true>), grid, dim3(kRopeThreads), 0, stream, Q,
-                       qs, K, ks, Vv, vs, QO, KO, VO, pos, tc, ts, N, p->p.H);
-  else if (half)
-    hipLaunchKernelGGL((rope_kernel<T, D, true, false>), grid, dim3(kRopeThreads), 0, stream, Q,
-                       qs, K, ks, Vv, vs, QO, KO, VO, pos, tc, ts, N, p->p.H);
-  else if (paired)
-    hipLaunchKernelGGL((rope_kernel<T, D, false, true>), grid, dim3(kRopeThreads), 0, stream, Q,
-                       qs, K, ks, Vv, vs, QO, KO, VO, pos, tc, ts, N, p->p.H);
-  else
-    hipLaunchKernelGGL((rope_kernel<T, D, false, false>), grid, dim3(kRopeThreads), 0, stream, Q,
-                       qs, K, ks, Vv, vs, QO, KO, VO, pos, tc, ts, N, p->p.H);
+  const int pm = p->p.paired;
+#define ROPE_LAUNCH(HF, PMV)                                                                   \
+  hipLaunchKernelGGL((rope_kernel<T, D, HF, PMV>), grid, dim3(kRopeThreads), 0, stream, Q, qs, K, \
+                     ks, Vv, vs, QO, KO, VO, pos, tc, ts, N, p->p.H)
+  if (half) {
+    if (pm == 0) ROPE_LAUNCH(true, 0);
+    else if (pm == 1) ROPE_LAUNCH(true, 1);
+    else ROPE_LAUNCH(true, 2);
+  } else {
+    if (pm == 0) ROPE_LAUNCH(false, 0);
+    else if (pm == 1) ROPE_LAUNCH(false, 1);
+    else ROPE_LAUNCH(false, 2);
+  }
+#undef ROPE_LAUNCH
   return hipGetLastError();
 }
 
