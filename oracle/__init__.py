@@ -145,3 +145,42 @@ def attn_bwd_sampled(q, k, v, dout, cu, q_rows, k_cols, paired=0, causal=1, wind
                                            _p(k_cols, _I64), _p(dk), _p(dv)),
            "oracle_attn_bwd_sampled")
     return dq, dk, dv
+
+
+# ------------------------------------------------------------ grouped query --
+# "Upgrading a textbook decoder" (juejin.cn), section 4 "GQA & FlashAttention":
+# the query heads form groups that share one K/V head; the module repeats each
+# of the Hkv K/V heads H / Hkv times along the head axis (repeat_interleave) and
+# then runs ordinary multi-head attention.  The oracle takes the same two
+# steps: expand (a plain index copy), then the fp64 attention above.  The
+# backward of the expansion sums the expanded heads' gradients over each group.
+
+def expand_kv(x, H):
+    """[N, Hkv, d] -> [N, H, d]: query head h reads K/V head h // (H / Hkv)."""
+    x = _f64(x)
+    Hkv = x.shape[1]
+    if H % Hkv:
+        raise ValueError("query heads must be a multiple of K/V heads")
+    return np.repeat(x, H // Hkv, axis=1)
+
+
+def attn_fwd_gqa(q, k, v, cu, causal=1, window=0, scale=0.0):
+    """O [N, H, d], LSE [H, N] with K, V of shape [N, Hkv, d]."""
+    H = np.shape(q)[1]
+    return attn_fwd(q, expand_kv(k, H), expand_kv(v, H), cu, 0, causal, window, scale)
+
+
+def attn_fwd_rows_gqa(q, k, v, cu, rows, causal=1, window=0, scale=0.0):
+    """Forward at selected (query head, token) rows with K, V of shape [N, Hkv, d]."""
+    H = np.shape(q)[1]
+    return attn_fwd_rows(q, expand_kv(k, H), expand_kv(v, H), cu, rows, 0, causal, window, scale)
+
+
+def attn_bwd_gqa(q, k, v, dout, cu, causal=1, window=0, scale=0.0):
+    """dQ [N, H, d]; dK, dV [N, Hkv, d] (each K/V head gathers its group's gradients)."""
+    H = np.shape(q)[1]
+    N, Hkv, d = np.shape(k)
+    dq, dke, dve = attn_bwd(q, expand_kv(k, H), expand_kv(v, H), dout, cu, 0, causal, window,
+                            scale)
+    G = H // Hkv
+    return dq, dke.reshape(N, Hkv, G, d).sum(axis=2), dve.reshape(N, Hkv, G, d).sum(axis=2)
