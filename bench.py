@@ -1,7 +1,7 @@
 """Benchmark of the rotary causal self-attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--paired P]
-                    [--no-cpu-baseline]
+                    [--kv-heads G] [--no-cpu-baseline]
 
 One step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: rope_qkv (Q, K rotated), attn_fwd (O, LSE) and, for
@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--paired", type=int, choices=(0, 1, 2), default=None,
                     help="override the workload's head pairing (2: adjacent partner h^1, "
                          "where rope_qkv also copies V in the slot layout)")
+    ap.add_argument("--kv-heads", type=int, default=None,
+                    help="grouped-query attention: number of K/V heads (divides the heads)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -98,6 +100,11 @@ def cpu_baseline(w, inp, seconds):
     def rows_sample(nrows):
         return np.stack([rng.integers(0, Hs, nrows), rng.integers(0, Ns, nrows)], 1)
 
+    def fwd_rows(qr, kr, rows):
+        if w.kv_heads and w.kv_heads != w.heads:
+            return oracle.attn_fwd_rows_gqa(qr, kr, v, cu, rows, w.causal, w.window, w.scale)
+        return oracle.attn_fwd_rows(qr, kr, v, cu, rows, w.paired, w.causal, w.window, w.scale)
+
     # calibrate: the RoPE of every token is a fixed cost, rows scale linearly
     t0 = time.perf_counter()
     qr = oracle.rope(q, cu, w.rope, w.rope_base, w.paired)
@@ -107,8 +114,7 @@ def cpu_baseline(w, inp, seconds):
     t_probe = []
     for probe in (512, 2048):
         t0 = time.perf_counter()
-        oracle.attn_fwd_rows(qr, kr, v, cu, rows_sample(probe), w.paired, w.causal, w.window,
-                             w.scale)
+        fwd_rows(qr, kr, rows_sample(probe))
         t_probe.append(time.perf_counter() - t0)
     per_row = max((t_probe[1] - t_probe[0]) / 1536, 1e-7)
     fixed = max(t_probe[0] - 512 * per_row, 0.0)
@@ -118,7 +124,7 @@ def cpu_baseline(w, inp, seconds):
     t0 = time.perf_counter()
     qr = oracle.rope(q, cu, w.rope, w.rope_base, w.paired)
     kr = oracle.rope(k, cu, w.rope, w.rope_base, w.paired)
-    oracle.attn_fwd_rows(qr, kr, v, cu, rows, w.paired, w.causal, w.window, w.scale)
+    fwd_rows(qr, kr, rows)
     dt = time.perf_counter() - t0
     flops = sum(4.0 * w.head_dim * visible(int(s)) for s in rows[:, 1])
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
@@ -142,6 +148,9 @@ def main():
     if args.paired is not None:
         import dataclasses
         w = dataclasses.replace(w, paired=args.paired)
+    if args.kv_heads is not None:
+        import dataclasses
+        w = dataclasses.replace(w, kv_heads=args.kv_heads)
     copy_v = w.paired == 2      # V' must be written in the slot layout
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -149,7 +158,8 @@ def main():
     plan = tca.attn_plan_create(w.n_tokens, w.heads, w.head_dim,
                                 "fp32" if w.dtype == wl.DTYPE_FP32 else "bf16", inp["cu"],
                                 causal=w.causal, window=w.window, softmax_scale=w.scale,
-                                rope=w.rope, rope_base=w.rope_base, paired=w.paired).bind(dev)
+                                rope=w.rope, rope_base=w.rope_base, paired=w.paired,
+                                num_kv_heads=w.kv_heads).bind(dev)
     info = plan.info
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
     do = inp["do"].to(dev) if w.backward else None
@@ -167,7 +177,7 @@ def main():
     rope()
     tca.attn_fwd(plan, q2, k2, v2, o, lse)
     if w.backward:
-        grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+        grads = tuple(torch.empty(x.shape, dtype=torch.float32, device=dev) for x in (q, k, v))
         try:
             tca.attn_bwd(plan, q2, k2, v2, o, lse, do, *grads)
         except tca.AttnError as e:
@@ -213,7 +223,8 @@ def main():
 
     kern_ms = {n: sum(a.elapsed_time(b) for a, b in events[n]) / len(events[n]) for n in names}
     digest = kernel_sources_digest()
-    wname = f"problem{w.num}" + ("" if args.paired is None else f"-paired{w.paired}")
+    wname = f"problem{w.num}" + ("" if args.paired is None else f"-paired{w.paired}") + (
+        "" if args.kv_heads is None else f"-kv{w.kv_heads}")
     # rope_qkv algorithmic bytes: Q, K read and written (plus V when copied)
     rope_bytes = info["rope_bytes"] * (1.5 if copy_v else 1.0)
     step_flops = info["fwd_flops"] + (info["bwd_flops"] if grads is not None else 0.0)
@@ -253,6 +264,7 @@ def main():
         "config": {"workload": w.name, "tokens": w.n_tokens, "heads": w.heads,
                    "head_dim": w.head_dim, "sequences": len(inp["cu"]) - 1,
                    "window": w.window, "paired": w.paired, "v_copied_by_rope": copy_v,
+                   "kv_heads": w.kv_heads or w.heads,
                    "rope": {1: "half-split", 2: "adjacent"}.get(w.rope, "none"),
                    "step": "+".join(names), "parallelism": "single GPU"},
         "roofline": roof,

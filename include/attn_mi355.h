@@ -24,7 +24,10 @@
  *        2t + (h mod 2).
  *  - "Upgrading a textbook decoder" (juejin.cn): section 2 "RoPE" -- the
  *    frequencies base^(-2i/d) and the half-split rotation; section 4 --
- *    FlashAttention computes the same result as the plain definition.
+ *    FlashAttention computes the same result as the plain definition, and
+ *    grouped-query attention: groups of query heads share one K/V head
+ *    (query head h reads K/V head h / (H / Hkv), the page's repetition of
+ *    each K/V head along the head axis, done here by indexing, not copying).
  *  - "SingleHeadAttention" note (ranhao.site) -- the lower-triangular causal
  *    mask; "mHC module" article (lshu.cn), sections 2.1-2.2 -- softmax with
  *    max subtraction.
@@ -39,8 +42,10 @@
  *                      hold token t's heads in the order 0, 2, 4, ..., 1, 3, 5,
  *                      ...: head h at position (h mod 2) * H/2 + h / 2 of the
  *                      token's H*d row.
+ *   K, V (grouped)     [N, Hkv, d] when num_kv_heads = Hkv < H (unpaired only).
  *   LSE                float [H', N'] (attention head, slot); natural log.
- *   dQ, dK, dV         float [N, H, d] (same slot view as Q when paired).
+ *   dQ, dK, dV         float [N, H, d] (same slot view as Q when paired);
+ *                      dK, dV are [N, Hkv, d] when grouped.
  *   N' = 2N, H' = H/2 when paired; else N' = N, H' = H.
  *
  * Conventions for every call:
@@ -97,6 +102,9 @@ typedef struct {
   double rope_base;          /* frequencies base^(-2i/d); e.g. 10000 */
   int32_t paired;            /* ATTN_UNPAIRED, ATTN_PAIRED (partner h + H/2, the
                                 memory view) or ATTN_PAIRED_ADJACENT (partner h ^ 1) */
+  int32_t num_kv_heads;      /* Hkv: 0 or H for one K/V head per query head; else a
+                                divisor of H (grouped-query attention, unpaired
+                                only: ATTN_E_UNSUPPORTED with pairing) */
 } attn_problem;
 
 /* Counts for throughput and roofline reporting (exact, from the plan). */
@@ -112,6 +120,7 @@ typedef struct {
   int64_t slots;             /* N' */
   int32_t attn_heads;        /* H' */
   int32_t max_positions;     /* rows of the rotary table */
+  int32_t kv_heads;          /* K/V heads: Hkv, or H' when not grouped */
 } attn_plan_info;
 
 /*
@@ -144,7 +153,9 @@ attn_status attn_plan_stats(const attn_plan *plan, attn_plan_info *info);
  * scheduling analysis.  which = 0: forward items (256 query slots each for
  * bf16, 128 for fp32 and for windows of at most 512 slots); which = 1:
  * backward key-tile items (128 key slots); which = 2: backward dQ items (128
- * query slots).  The backward lists are empty for fp32 problems.
+ * query slots).  The backward lists are empty for fp32 problems.  The head
+ * of every item is a query (attention) head; with grouped K/V heads the key
+ * tiles of a group's query heads add into the same dK/dV rows.
  * Each item is 8 int32: {attention head, r0, r1, s0, s1, stream, 0, 0}
  * where stream numbers the (attention head, sequence) pairs.  The list order
  * is the launch order: item i runs as workgroup i, on XCD i mod 8; items of one
@@ -163,12 +174,14 @@ attn_status attn_plan_work_items(const attn_plan *plan, int32_t which, int32_t *
  * token t of its sequence, head h, is rotated by angle p * base^(-2i/d) on
  * pair i, p = t (unpaired) or 2t + (h mod 2) (paired):
  *     (a, b) -> (a cos - b sin, b cos + a sin).
- * q, k: [N, H, d] with token strides q_tok_stride, k_tok_stride (elements,
- * >= H*d; e.g. 3*H*d for a packed [N, 3, H, d] QKV).  q_out, k_out: dense
- * [N, H, d]; q_out == q (in place) is allowed when q_tok_stride == H*d, same
- * for k.  Written dense, the outputs already are the paired interleaved layout.
- * v / v_out: when v_out is not NULL, V (token stride v_tok_stride) is copied
- * dense into v_out in the same pass; when v_out is NULL, v is ignored.
+ * q: [N, H, d], k: [N, Hkv, d] with token strides q_tok_stride >= H*d,
+ * k_tok_stride >= Hkv*d (elements; e.g. 3*H*d for a packed [N, 3, H, d]
+ * QKV).  q_out, k_out: dense [N, H, d] and [N, Hkv, d]; q_out == q (in place)
+ * is allowed when q_tok_stride == H*d, same for k.  Written dense, the outputs
+ * already are the paired interleaved layout.
+ * v / v_out: when v_out is not NULL, V ([N, Hkv, d], token stride
+ * v_tok_stride) is copied dense into v_out in the same pass; when v_out is
+ * NULL, v is ignored.
  * ATTN_PAIRED_ADJACENT: the outputs are written in that layout's head order
  * (see Layouts), so v_out is required (V' feeds attn_fwd) and neither output
  * may alias its input (ATTN_E_INVALID otherwise).
@@ -181,8 +194,9 @@ attn_status rope_qkv(const attn_plan *plan, const void *q, int64_t q_tok_stride,
 /*
  * Forward attention over the plan's sequences and mask (flash-style: the
  * N' x N' score matrix never reaches HBM; "Upgrading a textbook decoder",
- * section 4).  q, k, v, o: dense [N, H, d] in the plan's dtype (q, k already
- * rotated); lse: float [H', N'].  Every slot of o and lse is written.
+ * section 4).  q, o: dense [N, H, d], k, v: dense [N, Hkv, d], in the plan's
+ * dtype (q, k already rotated); lse: float [H', N'].  Every slot of o and lse
+ * is written.
  */
 attn_status attn_fwd(const attn_plan *plan, const void *q, const void *k, const void *v, void *o,
                      float *lse, void *stream);
@@ -192,8 +206,13 @@ attn_status attn_fwd(const attn_plan *plan, const void *q, const void *k, const 
  * values), recomputing P = exp(s q k^T - LSE):
  *     D_i = dO_i . O_i,  dS = P o (dO V^T - D),
  *     dV = P^T dO,  dQ = s dS K,  dK = s dS^T Q.
- * q, k, v, o, d_o: dense [N, H, d] in the plan's dtype; lse: float [H', N']
- * as written by attn_fwd; dq, dk, dv: float [N, H, d], fully overwritten.
+ * q, o, d_o: dense [N, H, d], k, v: dense [N, Hkv, d], in the plan's dtype;
+ * lse: float [H', N'] as written by attn_fwd; dq: float [N, H, d], dk, dv:
+ * float [N, Hkv, d], fully overwritten.  With grouped K/V heads, dK and dV of
+ * a K/V head sum the contributions of every query head of its group (float
+ * atomic adds, so their rounding order may differ between runs; without
+ * grouping every output element is written once and results are
+ * bit-reproducible).
  * bf16 only (ATTN_E_UNSUPPORTED for fp32).  Uses the workspace's scratch
  * area, so two attn_bwd calls sharing one workspace must not overlap.
  */

@@ -34,7 +34,8 @@ def make_plan(w, cu, device="cuda"):
     return tca.attn_plan_create(w.n_tokens, w.heads, w.head_dim,
                                 "fp32" if w.dtype == wl.DTYPE_FP32 else "bf16", cu,
                                 causal=w.causal, window=w.window, softmax_scale=w.scale,
-                                rope=w.rope, rope_base=w.rope_base, paired=w.paired).bind(device)
+                                rope=w.rope, rope_base=w.rope_base, paired=w.paired,
+                                num_kv_heads=w.kv_heads).bind(device)
 
 
 def f64(t):

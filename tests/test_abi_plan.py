@@ -62,6 +62,9 @@ def plan(**kw):
     (dict(softmax_scale=-1.0), -1),
     (dict(paired=3, num_heads=4), -1),
     (dict(paired=2, num_heads=3), -1),                 # odd heads, adjacent pairing
+    (dict(num_heads=6, num_kv_heads=4), -1),           # K/V heads must divide H
+    (dict(num_heads=6, num_kv_heads=-1), -1),
+    (dict(num_heads=6, num_kv_heads=3, paired=1), -2), # grouped K/V heads are unpaired only
     (dict(head_dim=32), -2),                           # valid, not covered by the kernels
     (dict(head_dim=96), -2),
 ])
@@ -99,6 +102,34 @@ def test_item_sizes_follow_the_dtype():
     for bad in (-1, 3):
         with pytest.raises(tca.AttnError):
             pb.work_items(bad)
+
+
+@pytest.mark.parametrize("H,Hkv,window", [(6, 2, 0), (8, 1, 100), (4, 4, 0)])
+def test_grouped_kv_work_lists(H, Hkv, window):
+    # forward, dQ and dK/dV items all run per query head (the dK/dV items of a
+    # group add into their K/V head's rows); the query heads of a group are
+    # interleaved so items reading the same K/V rows share an XCD (position i
+    # runs on XCD i % 8)
+    cu = list(range(0, 3073, 256)) + [3300]
+    N = cu[-1]
+    p = plan(num_tokens=N, num_heads=H, num_kv_heads=Hkv, cu_seqlens=cu, window=window)
+    mask = brute.dense_mask(cu, 1, 1, window)
+    assert p.info["kv_heads"] == Hkv and p.info["attn_heads"] == H
+    assert p.info["visible_pairs"] == H * int(mask.sum())
+    elems, kv = N * H * 64, N * Hkv * 64
+    assert p.info["rope_bytes"] == 2 * (elems + kv) * 2
+    for which, heads in ((0, H), (2, H), (1, H)):
+        seen = np.zeros((heads, N), dtype=int)
+        for head, r0, r1, *_ in p.work_items(which):
+            seen[head, r0:r1] += 1
+        assert (seen == 1).all(), which
+    fwd = p.work_items(0)
+    xcds = {}
+    for i, it in enumerate(fwd):
+        xcds.setdefault((int(it[5]), int(it[1])), set()).add(i % 8)
+    # (the tail of the list borrows items across XCDs to balance load)
+    assert sum(len(x) == 1 for x in xcds.values()) >= 0.6 * len(xcds)
+    assert {int(it[0]) // (H // Hkv) for it in fwd if it[5] == fwd[0][5]} == {fwd[0][0] // (H // Hkv)}
 
 
 def dense_pairs(cu, mult, causal, window):

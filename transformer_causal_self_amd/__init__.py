@@ -47,7 +47,8 @@ class _Problem(ctypes.Structure):
                 ("cu_seqlens", ctypes.POINTER(ctypes.c_int32)), ("num_seqs", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("rope", ctypes.c_int32),
-                ("rope_base", ctypes.c_double), ("paired", ctypes.c_int32)]
+                ("rope_base", ctypes.c_double), ("paired", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32)]
 
 
 class _Info(ctypes.Structure):
@@ -56,7 +57,7 @@ class _Info(ctypes.Structure):
                 ("fwd_bytes", ctypes.c_double), ("bwd_bytes", ctypes.c_double),
                 ("fwd_items", ctypes.c_int64), ("bwd_items", ctypes.c_int64),
                 ("slots", ctypes.c_int64), ("attn_heads", ctypes.c_int32),
-                ("max_positions", ctypes.c_int32)]
+                ("max_positions", ctypes.c_int32), ("kv_heads", ctypes.c_int32)]
 
 
 _lib = None
@@ -163,7 +164,8 @@ class Plan:
 
 def attn_plan_create(num_tokens: int, num_heads: int, head_dim: int, dtype, cu_seqlens,
                      causal: int = 1, window: int = 0, softmax_scale: float = 0.0, rope="half",
-                     rope_base: float = 10000.0, paired: int = 0) -> Plan:
+                     rope_base: float = 10000.0, paired: int = 0,
+                     num_kv_heads: int = 0) -> Plan:
     if isinstance(dtype, str):
         dtype = {"bf16": ATTN_BF16, "fp32": ATTN_FP32}[dtype]
     elif isinstance(dtype, torch.dtype):
@@ -173,13 +175,13 @@ def attn_plan_create(num_tokens: int, num_heads: int, head_dim: int, dtype, cu_s
                   cu_seqlens=cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                   num_seqs=len(cu) - 1, causal=causal, window=window,
                   softmax_scale=softmax_scale, rope=ROPE.get(rope, rope), rope_base=rope_base,
-                  paired=paired)
+                  paired=paired, num_kv_heads=num_kv_heads)
     h = ctypes.c_void_p()
     _check("attn_plan_create", load_library().attn_plan_create(ctypes.byref(pr), ctypes.byref(h)))
     problem = dict(num_tokens=num_tokens, num_heads=num_heads, head_dim=head_dim, dtype=dtype,
                    cu_seqlens=cu.copy(), causal=causal, window=window,
                    softmax_scale=softmax_scale, rope=ROPE.get(rope, rope), rope_base=rope_base,
-                   paired=paired)
+                   paired=paired, num_kv_heads=num_kv_heads or num_heads)
     return Plan(h.value, problem)
 
 
@@ -190,32 +192,34 @@ def _token_stride(x: torch.Tensor, H: int, d: int) -> int:
     return x.stride(0)
 
 
-def _need(plan: Plan, x: torch.Tensor, name: str, dtype=None, dense=True):
+def _need(plan: Plan, x: torch.Tensor, name: str, dtype=None, dense=True, kv=False):
     p = plan.problem
+    heads = p["num_kv_heads"] if kv else p["num_heads"]
     if plan.workspace is None:
         raise AttnError(name, -4)
     if not x.is_cuda or x.device != plan.workspace.device:
         raise ValueError(f"{name} must be on {plan.workspace.device}")
     if x.dtype != (dtype or plan.dtype):
         raise ValueError(f"{name} must be {dtype or plan.dtype}, got {x.dtype}")
-    if dense and (tuple(x.shape) != (p["num_tokens"], p["num_heads"], p["head_dim"])
+    if dense and (tuple(x.shape) != (p["num_tokens"], heads, p["head_dim"])
                   or not x.is_contiguous()):
-        raise ValueError(f"{name} must be contiguous [N, H, d]")
+        raise ValueError(f"{name} must be contiguous [N, {'Hkv' if kv else 'H'}, d]")
 
 
 def rope_qkv(plan: Plan, q, k, v=None, q_out=None, k_out=None, v_out=None):
     """Rotate Q and K (and densify V if v_out is given).  Returns (q', k'[, v'])."""
     p = plan.problem
-    H, d = p["num_heads"], p["head_dim"]
+    H, Hkv, d = p["num_heads"], p["num_kv_heads"], p["head_dim"]
     for name, x in (("q", q), ("k", k)) + ((("v", v),) if v_out is not None else ()):
         _need(plan, x, name, dense=False)
-    qs, ks = _token_stride(q, H, d), _token_stride(k, H, d)
-    vs = _token_stride(v, H, d) if v_out is not None else 0
+    qs, ks = _token_stride(q, H, d), _token_stride(k, Hkv, d)
+    vs = _token_stride(v, Hkv, d) if v_out is not None else 0
     q_out = torch.empty((q.shape[0], H, d), dtype=q.dtype, device=q.device) if q_out is None else q_out
-    k_out = torch.empty((k.shape[0], H, d), dtype=k.dtype, device=k.device) if k_out is None else k_out
-    for name, x in (("q_out", q_out), ("k_out", k_out)) + (
-            (("v_out", v_out),) if v_out is not None else ()):
-        _need(plan, x, name)
+    k_out = torch.empty((k.shape[0], Hkv, d), dtype=k.dtype, device=k.device) if k_out is None \
+        else k_out
+    for name, x, kv in (("q_out", q_out, False), ("k_out", k_out, True)) + (
+            (("v_out", v_out, True),) if v_out is not None else ()):
+        _need(plan, x, name, kv=kv)
     _check("rope_qkv", load_library().rope_qkv(
         plan.handle, q.data_ptr(), qs, k.data_ptr(), ks,
         v.data_ptr() if v_out is not None else None, vs, q_out.data_ptr(), k_out.data_ptr(),
@@ -225,8 +229,8 @@ def rope_qkv(plan: Plan, q, k, v=None, q_out=None, k_out=None, v_out=None):
 
 def attn_fwd(plan: Plan, q, k, v, o=None, lse=None):
     """O [N, H, d] (plan dtype) and LSE float32 [H', N']."""
-    for name, x in (("q", q), ("k", k), ("v", v)):
-        _need(plan, x, name)
+    for name, x, kv in (("q", q, False), ("k", k, True), ("v", v, True)):
+        _need(plan, x, name, kv=kv)
     info = plan.info
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((info["attn_heads"], info["slots"]), dtype=torch.float32,
@@ -242,14 +246,17 @@ def attn_fwd(plan: Plan, q, k, v, o=None, lse=None):
 
 
 def attn_bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None):
-    """dQ, dK, dV float32 [N, H, d] (gradients with respect to the rotated q, k and v)."""
-    for name, x in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
-        _need(plan, x, name)
+    """dQ float32 [N, H, d]; dK, dV float32 [N, Hkv, d] (gradients with respect to
+    the rotated q, k and v)."""
+    for name, x, kv in (("q", q, False), ("k", k, True), ("v", v, True), ("o", o, False),
+                        ("do", do, False)):
+        _need(plan, x, name, kv=kv)
     _need(plan, lse, "lse", torch.float32, dense=False)
-    mk = lambda t: torch.empty(q.shape, dtype=torch.float32, device=q.device) if t is None else t
-    dq, dk, dv = mk(dq), mk(dk), mk(dv)
-    for name, x in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _need(plan, x, name, torch.float32)
+    mk = lambda t, ref: torch.empty(ref.shape, dtype=torch.float32, device=q.device) \
+        if t is None else t
+    dq, dk, dv = mk(dq, q), mk(dk, k), mk(dv, v)
+    for name, x, kv in (("dq", dq, False), ("dk", dk, True), ("dv", dv, True)):
+        _need(plan, x, name, torch.float32, kv=kv)
     _check("attn_bwd", load_library().attn_bwd(plan.handle, q.data_ptr(), k.data_ptr(),
                                                v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                                do.data_ptr(), dq.data_ptr(), dk.data_ptr(),

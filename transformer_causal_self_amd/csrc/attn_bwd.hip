@@ -148,15 +148,19 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dkv_kernel(
     const WorkItem *__restrict__ items, const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const __bf16 *__restrict__ V, const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
     const float *__restrict__ delta, float *__restrict__ dK, float *__restrict__ dV, int Hs,
-    int64_t Ns, float scale, float scale_log2, int causal, int window) {
+    int Hks, int G, int64_t Ns, float scale, float scale_log2, int causal, int window) {
   constexpr int RS = DkvSmem<D>::RS, TS = DkvSmem<D>::TS, BQ = kBwdBQ;
   __shared__ __attribute__((aligned(16))) DkvSmem<D> sm;
   const WorkItem it = items[blockIdx.x];  // keys [q0, q1), queries [k0, k1)
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int h = lane >> 5, l32 = lane & 31;
-  const int64_t rs = (int64_t)Hs * D;
+  // the item's head is a query head; with grouped K/V heads (G > 1) its
+  // K/V head is it.head / G, and the group's items add into dK and dV
+  const int64_t rs = (int64_t)Hs * D;    // Q / dO elements between consecutive slots
+  const int64_t rsk = (int64_t)Hks * D;  // K / V / dK / dV
   const int64_t ho = (int64_t)it.head * D;
+  const int64_t hk = (int64_t)(it.head / G) * D;
   const int wk0 = it.q0 + 32 * w, wk1 = min(wk0 + 32, it.q1);
   const int kj = wk0 + l32;  // this lane's key (column of S)
   const bool kok = kj < it.q1;
@@ -165,8 +169,8 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dkv_kernel(
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
     if (kok) {
-      kf[c] = load_bf16x8(K + ho + kj * rs + 16 * c + 8 * h);
-      vf[c] = load_bf16x8(V + ho + kj * rs + 16 * c + 8 * h);
+      kf[c] = load_bf16x8(K + hk + kj * rsk + 16 * c + 8 * h);
+      vf[c] = load_bf16x8(V + hk + kj * rsk + 16 * c + 8 * h);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) kf[c][e] = vf[c][e] = (__bf16)0.0f;
@@ -263,9 +267,14 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dkv_kernel(
     if (key < it.q1) {
 #pragma unroll
       for (int dl = 0; dl < D / 32; ++dl) {
-        const int64_t off = key * rs + ho + 32 * dl + l32;
-        dV[off] = dv[dl][r];
-        dK[off] = dk[dl][r] * scale;
+        const int64_t off = key * rsk + hk + 32 * dl + l32;
+        if (G == 1) {
+          dV[off] = dv[dl][r];
+          dK[off] = dk[dl][r] * scale;
+        } else {  // the group's query heads share this K/V row (zeroed first)
+          unsafeAtomicAdd(&dV[off], dv[dl][r]);
+          unsafeAtomicAdd(&dK[off], dk[dl][r] * scale);
+        }
       }
     }
   }
@@ -290,7 +299,8 @@ template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dq_kernel(
     const WorkItem *__restrict__ items, const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const __bf16 *__restrict__ V, const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
-    const float *__restrict__ delta, float *__restrict__ dQ, int Hs, int64_t Ns, float scale,
+    const float *__restrict__ delta, float *__restrict__ dQ, int Hs, int Hks, int G, int64_t Ns,
+    float scale,
     float scale_log2, int causal, int window) {
   constexpr int RS = DqSmem<D>::RS, TS = DqSmem<D>::TS, BK = kFwdBK;
   __shared__ __attribute__((aligned(16))) DqSmem<D> sm;
@@ -298,8 +308,10 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dq_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int h = lane >> 5, l32 = lane & 31;
-  const int64_t rs = (int64_t)Hs * D;
+  const int64_t rs = (int64_t)Hs * D;    // Q / dO / dQ elements between consecutive slots
+  const int64_t rsk = (int64_t)Hks * D;  // K / V
   const int64_t ho = (int64_t)it.head * D;
+  const int64_t hk = (int64_t)(it.head / G) * D;  // the query head's K/V head
   const int wq0 = it.q0 + 32 * w, wq1 = min(wq0 + 32, it.q1);
   const int qi = wq0 + l32;
   const bool qok = qi < it.q1;
@@ -323,13 +335,13 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dq_kernel(
 
   const int nk = (it.k1 - it.k0 + BK - 1) / BK;
   PairStage<D, 64 * NW> sk, sv;
-  sk.load(K + ho, rs, it.k0, it.k1, tid);
-  sv.load(V + ho, rs, it.k0, it.k1, tid);
+  sk.load(K + hk, rsk, it.k0, it.k1, tid);
+  sv.load(V + hk, rsk, it.k0, it.k1, tid);
   sk.store(sm.b[0].k, sm.b[0].kt, tid);
   sv.store(sm.b[0].v, nullptr, tid);
   if (nk > 1) {
-    sk.load(K + ho, rs, it.k0 + BK, it.k1, tid);
-    sv.load(V + ho, rs, it.k0 + BK, it.k1, tid);
+    sk.load(K + hk, rsk, it.k0 + BK, it.k1, tid);
+    sv.load(V + hk, rsk, it.k0 + BK, it.k1, tid);
   }
   __syncthreads();
   for (int t = 0; t < nk; ++t) {
@@ -379,8 +391,8 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dq_kernel(
       sk.store(sm.b[(t + 1) & 1].k, sm.b[(t + 1) & 1].kt, tid);
       sv.store(sm.b[(t + 1) & 1].v, nullptr, tid);
       if (t + 2 < nk) {
-        sk.load(K + ho, rs, kt0 + 2 * BK, it.k1, tid);
-        sv.load(V + ho, rs, kt0 + 2 * BK, it.k1, tid);
+        sk.load(K + hk, rsk, kt0 + 2 * BK, it.k1, tid);
+        sv.load(V + hk, rsk, kt0 + 2 * BK, it.k1, tid);
       }
     }
     __syncthreads();
@@ -394,6 +406,17 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dq_kernel(
         *reinterpret_cast<float4 *>(row + 32 * dl + 8 * b + 4 * h) =
             make_float4(dq[dl][4 * b] * scale, dq[dl][4 * b + 1] * scale,
                         dq[dl][4 * b + 2] * scale, dq[dl][4 * b + 3] * scale);
+  }
+}
+
+// Zero n floats (dK and dV before the grouped heads add into them; a kernel
+// rather than a memset, so the launch sequence stays graph-capturable).
+__global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ a, float *__restrict__ b,
+                                                   int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) {
+    a[i] = 0.0f;
+    b[i] = 0.0f;
   }
 }
 
@@ -412,14 +435,21 @@ hipError_t launch_typed(const attn_plan *p, const void *q, const void *k, const 
   constexpr int NWK = kBwdWaves, NWQ = kBwdWaves;
   hipLaunchKernelGGL((delta_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
                      O, G, delta, Hs, Ns);
+  if (p->p.G > 1) {
+    const int64_t n = p->p.Ns * p->p.Hks * D;
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, dk,
+                       dv, n);
+  }
   if (!p->bwd.empty())
     hipLaunchKernelGGL((dkv_kernel<D, NWK>), dim3((unsigned)p->bwd.size()), dim3(64 * NWK), 0,
                        stream, reinterpret_cast<const WorkItem *>(p->ws + p->off_bwd), Q, K, V, G,
-                       lse, delta, dk, dv, Hs, Ns, scale, scale_log2, p->p.causal, p->p.window);
+                       lse, delta, dk, dv, Hs, p->p.Hks, p->p.G, Ns, scale, scale_log2,
+                       p->p.causal, p->p.window);
   if (!p->dq.empty())
     hipLaunchKernelGGL((dq_kernel<D, NWQ>), dim3((unsigned)p->dq.size()), dim3(64 * NWQ), 0,
                        stream, reinterpret_cast<const WorkItem *>(p->ws + p->off_dq), Q, K, V, G,
-                       lse, delta, dq, Hs, Ns, scale, scale_log2, p->p.causal, p->p.window);
+                       lse, delta, dq, Hs, p->p.Hks, p->p.G, Ns, scale, scale_log2,
+                       p->p.causal, p->p.window);
   return hipGetLastError();
 }
 

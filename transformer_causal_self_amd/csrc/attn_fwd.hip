@@ -152,17 +152,18 @@ constexpr int fwd_min_blocks() {
 template <typename T, int D>
 __global__ __launch_bounds__(kFwdThreadsF32, fwd_min_blocks<T>()) void fwd_kernel(
     const WorkItem *__restrict__ items, const T *__restrict__ Q, const T *__restrict__ K,
-    const T *__restrict__ V, T *__restrict__ O, float *__restrict__ LSE, int Hs, int64_t Ns,
+    const T *__restrict__ V, T *__restrict__ O, float *__restrict__ LSE, int Hs, int Hks, int G, int64_t Ns,
     float scale, float scale_log2, int causal, int window) {
   __shared__ __attribute__((aligned(16))) Smem<T, D> sm;
   const WorkItem it = items[blockIdx.x];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int h = lane >> 5, l32 = lane & 31;
-  const int64_t rs = (int64_t)Hs * D;  // elements between consecutive slots
+  const int64_t rs = (int64_t)Hs * D;    // Q / O elements between consecutive slots
+  const int64_t rsk = (int64_t)Hks * D;  // K / V elements between consecutive slots
   const T *Qh = Q + (int64_t)it.head * D;
-  const T *Kh = K + (int64_t)it.head * D;
-  const T *Vh = V + (int64_t)it.head * D;
+  const T *Kh = K + (int64_t)(it.head / G) * D;  // the query head's K/V head
+  const T *Vh = V + (int64_t)(it.head / G) * D;
 
   const int wq0 = it.q0 + 32 * w;             // first query of this wave
   const int wq1 = min(wq0 + 32, it.q1);        // one past its last valid query
@@ -180,13 +181,13 @@ __global__ __launch_bounds__(kFwdThreadsF32, fwd_min_blocks<T>()) void fwd_kerne
 
   const int nk = (it.k1 - it.k0 + BK - 1) / BK;
   Stage<T, D> st;
-  st.load(Kh, Vh, rs, it.k0, it.k1, tid);
+  st.load(Kh, Vh, rsk, it.k0, it.k1, tid);
   for (int t = 0; t < nk; ++t) {
     const int kt0 = it.k0 + t * BK;
     __syncthreads();
     st.store(sm, tid);
     __syncthreads();
-    if (t + 1 < nk) st.load(Kh, Vh, rs, kt0 + BK, it.k1, tid);
+    if (t + 1 < nk) st.load(Kh, Vh, rsk, kt0 + BK, it.k1, tid);
 
     // wave-uniform tile classification
     const bool active = wq0 < wq1 && !(causal && kt0 > wq1 - 1) &&
@@ -365,17 +366,18 @@ template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
     const WorkItem *__restrict__ items, const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const __bf16 *__restrict__ V, __bf16 *__restrict__ O, float *__restrict__ LSE, int Hs,
-    int64_t Ns, float scale, float scale_log2, int causal, int window) {
+    int Hks, int G, int64_t Ns, float scale, float scale_log2, int causal, int window) {
   constexpr int KS = SmemBF<D>::KS, VS = SmemBF<D>::VS;
   __shared__ __attribute__((aligned(16))) SmemBF<D> sm;
   const WorkItem it = items[blockIdx.x];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int h = lane >> 5, l32 = lane & 31;
-  const int64_t rs = (int64_t)Hs * D;  // elements between consecutive slots
-  const uint32_t rsb = (uint32_t)rs * 2u;
-  const __bf16 *Kh = K + (int64_t)it.head * D;
-  const __bf16 *Vh = V + (int64_t)it.head * D;
+  const int64_t rs = (int64_t)Hs * D;    // Q / O elements between consecutive slots
+  const int64_t rsk = (int64_t)Hks * D;  // K / V elements between consecutive slots
+  const uint32_t rsbq = (uint32_t)rs * 2u, rsb = (uint32_t)rsk * 2u;
+  const __bf16 *Kh = K + (int64_t)(it.head / G) * D;  // the query head's K/V head
+  const __bf16 *Vh = V + (int64_t)(it.head / G) * D;
 
   const int wq0 = it.q0 + 32 * w;       // first query of this wave
   const int wq1 = min(wq0 + 32, it.q1);  // one past its last valid query
@@ -386,10 +388,10 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
   bf16x8 qf[D / 16];
   {
     const auto rq = make_rsrc(Q + (int64_t)wq0 * rs + (int64_t)it.head * D,
-                              (uint32_t)max(0, wq1 - wq0) * rsb);
+                              (uint32_t)max(0, wq1 - wq0) * rsbq);
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
-      qf[c] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)l32 * rsb + 32u * c + 16u * h));
+      qf[c] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)l32 * rsbq + 32u * c + 16u * h));
   }
 
   floatx16 o[D / 32];
@@ -403,10 +405,10 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
   const int nk = (it.k1 - it.k0 + BK - 1) / BK;
   constexpr int NT = 64 * NW;
   StageBF<D, NT> st;
-  st.load(Kh + (int64_t)it.k0 * rs, Vh + (int64_t)it.k0 * rs, it.k1 - it.k0, rsb, tid);
+  st.load(Kh + (int64_t)it.k0 * rsk, Vh + (int64_t)it.k0 * rsk, it.k1 - it.k0, rsb, tid);
   st.store(sm.k[0], sm.vt[0], tid);
   if (nk > 1)
-    st.load(Kh + (int64_t)(it.k0 + BK) * rs, Vh + (int64_t)(it.k0 + BK) * rs,
+    st.load(Kh + (int64_t)(it.k0 + BK) * rsk, Vh + (int64_t)(it.k0 + BK) * rsk,
             it.k1 - it.k0 - BK, rsb, tid);
   __syncthreads();
 
@@ -504,7 +506,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
     if (t + 1 < nk) {
       st.store(sm.k[buf ^ 1], sm.vt[buf ^ 1], tid);
       if (t + 2 < nk)
-        st.load(Kh + (int64_t)(kt0 + 2 * BK) * rs, Vh + (int64_t)(kt0 + 2 * BK) * rs,
+        st.load(Kh + (int64_t)(kt0 + 2 * BK) * rsk, Vh + (int64_t)(kt0 + 2 * BK) * rsk,
                 it.k1 - kt0 - 2 * BK, rsb, tid);
     }
     __syncthreads();
@@ -536,22 +538,23 @@ hipError_t launch_typed(const attn_plan *p, const void *q, const void *k, const 
   if (n == 0) return hipSuccess;
   const float scale = p->p.scale;
   const float scale_log2 = scale * 1.4426950408889634f;
+  const Problem &P = p->p;
   if (std::is_same<T, __bf16>::value && p->fwd_bq == kFwdBQ)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, kFwdBQ / 32>), dim3(n), dim3(2 * kFwdBQ), 0, stream,
                        items, static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
-                       static_cast<const __bf16 *>(v), static_cast<__bf16 *>(o), lse, p->p.Hs,
-                       p->p.Ns, scale, scale_log2, p->p.causal, p->p.window);
+                       static_cast<const __bf16 *>(v), static_cast<__bf16 *>(o), lse, P.Hs, P.Hks,
+                       P.G, P.Ns, scale, scale_log2, P.causal, P.window);
   else if (std::is_same<T, __bf16>::value)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, kFwdBQShort / 32>), dim3(n), dim3(2 * kFwdBQShort), 0,
                        stream, items, static_cast<const __bf16 *>(q),
                        static_cast<const __bf16 *>(k), static_cast<const __bf16 *>(v),
-                       static_cast<__bf16 *>(o), lse, p->p.Hs, p->p.Ns, scale, scale_log2,
-                       p->p.causal, p->p.window);
+                       static_cast<__bf16 *>(o), lse, P.Hs, P.Hks, P.G, P.Ns, scale, scale_log2,
+                       P.causal, P.window);
   else
     hipLaunchKernelGGL((fwd_kernel<float, D>), dim3(n), dim3(kFwdThreadsF32), 0, stream, items,
                        static_cast<const float *>(q), static_cast<const float *>(k),
-                       static_cast<const float *>(v), static_cast<float *>(o), lse, p->p.Hs,
-                       p->p.Ns, scale, scale_log2, p->p.causal, p->p.window);
+                       static_cast<const float *>(v), static_cast<float *>(o), lse, P.Hs, P.Hks,
+                       P.G, P.Ns, scale, scale_log2, P.causal, P.window);
   return hipGetLastError();
 }
 

@@ -56,8 +56,11 @@ struct Problem {
   int32_t rope;
   double rope_base;
   int32_t paired;
-  int32_t Hs;      // attention heads
+  int32_t Hs;      // attention (query) heads
   int64_t Ns;      // slots
+  int32_t Hkv;     // K/V heads given (= H unless grouped)
+  int32_t Hks;     // K/V attention heads (= Hs unless grouped)
+  int32_t G;       // query heads per K/V head: Hs / Hks
 };
 
 }  // namespace attn

@@ -169,7 +169,10 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
     if (cu[i + 1] < cu[i]) return ATTN_E_INVALID;
     max_len = std::max<int64_t>(max_len, cu[i + 1] - cu[i]);
   }
+  const int Hkv = pr->num_kv_heads == 0 ? pr->num_heads : pr->num_kv_heads;
+  if (Hkv < 1 || pr->num_heads % Hkv) return ATTN_E_INVALID;
   if (pr->head_dim != 64 && pr->head_dim != 128) return ATTN_E_UNSUPPORTED;
+  if (Hkv != pr->num_heads && pr->paired) return ATTN_E_UNSUPPORTED;
 
   attn_plan *p = new (std::nothrow) attn_plan();
   if (!p) return ATTN_E_NOMEM;
@@ -187,6 +190,9 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
     P.rope_base = pr->rope_base;
     P.paired = pr->paired;
     P.Hs = pr->paired ? P.H / 2 : P.H;
+    P.Hkv = Hkv;
+    P.Hks = pr->paired ? P.Hs : Hkv;
+    P.G = P.Hs / P.Hks;
     P.Ns = P.N * mult;
     p->cu.assign(cu, cu + S + 1);
 
@@ -220,36 +226,60 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
     p->fwd_bq = !bf16 ? attn::kFwdBQF32
                 : (P.window > 0 && P.window <= attn::kFwdShortWindow) ? attn::kFwdBQShort
                                                                       : attn::kFwdBQ;
-    for (int j = 0; j < P.Hs; ++j)
+    // One stream per (K/V head, sequence).  With grouped K/V heads, the items
+    // of the group's query heads are interleaved tile by tile, so the ones
+    // that read the same K/V rows land in one chunk (one XCD, one L2).
+    std::vector<std::vector<WorkItem>> tf(P.G), tq(P.G), tb(P.G);
+    auto interleave = [](std::vector<std::vector<WorkItem>> &parts, std::vector<WorkItem> &out) {
+      for (size_t i = 0;; ++i) {
+        bool any = false;
+        for (auto &v : parts)
+          if (i < v.size()) {
+            out.push_back(v[i]);
+            any = true;
+          }
+        if (!any) break;
+      }
+      for (auto &v : parts) v.clear();
+    };
+    for (int kh = 0; kh < P.Hks; ++kh)
       for (int s = 0; s < S; ++s) {
         const int64_t b = (int64_t)cu[s] * mult, e = (int64_t)cu[s + 1] * mult;
         if (e == b) continue;
-        pairs += visible_pairs_of(e - b, P.causal, P.window);
-        cut_items(p->fwd, j, stream, b, e, p->fwd_bq, P.causal, P.window, true);
-        if (bf16) {
-          cut_items(p->bwd, j, stream, b, e, attn::kBwdRows, P.causal, P.window, false);
-          cut_items(p->dq, j, stream, b, e, attn::kBwdRows, P.causal, P.window, true);
+        for (int g = 0; g < P.G; ++g) {
+          const int j = kh * P.G + g;  // query attention head
+          pairs += visible_pairs_of(e - b, P.causal, P.window);
+          cut_items(tf[g], j, stream, b, e, p->fwd_bq, P.causal, P.window, true);
+          if (bf16) {
+            cut_items(tq[g], j, stream, b, e, attn::kBwdRows, P.causal, P.window, true);
+            cut_items(tb[g], j, stream, b, e, attn::kBwdRows, P.causal, P.window, false);
+          }
         }
+        interleave(tf, p->fwd);
+        interleave(tq, p->dq);
+        interleave(tb, p->bwd);  // per query head; grouped heads add into dK/dV
         ++stream;
       }
     order_for_xcds(p->fwd, attn::kFwdBK, attn::kXcdChunk);
     order_for_xcds(p->bwd, attn::kBwdBQ, attn::kXcdChunk);
     order_for_xcds(p->dq, attn::kFwdBK, attn::kXcdChunk);
 
-    const double elems = (double)P.N * P.H * P.d;
+    const double elems = (double)P.N * P.H * P.d;      // Q, O, dO, dQ
+    const double kv_elems = (double)P.N * P.Hkv * P.d;  // K, V, dK, dV
     const double es = P.dtype == ATTN_BF16 ? 2.0 : 4.0;
     const double lse_bytes = 4.0 * (double)P.Ns * P.Hs;
     attn_plan_info &I = p->info;
     I.visible_pairs = pairs;
     I.fwd_flops = 4.0 * P.d * (double)pairs;
     I.bwd_flops = 2.5 * I.fwd_flops;
-    I.rope_bytes = 4.0 * elems * es;
-    I.fwd_bytes = 4.0 * elems * es + lse_bytes;
-    I.bwd_bytes = 5.0 * elems * es + lse_bytes + 3.0 * elems * 4.0;
+    I.rope_bytes = 2.0 * (elems + kv_elems) * es;
+    I.fwd_bytes = 2.0 * (elems + kv_elems) * es + lse_bytes;
+    I.bwd_bytes = (3.0 * elems + 2.0 * kv_elems) * es + lse_bytes + (elems + 2.0 * kv_elems) * 4.0;
     I.fwd_items = (int64_t)p->fwd.size();
     I.bwd_items = (int64_t)p->bwd.size();
     I.slots = P.Ns;
     I.attn_heads = P.Hs;
+    I.kv_heads = P.Hks;
     I.max_positions = p->max_pos;
 
     // Workspace layout.
@@ -332,15 +362,16 @@ attn_status rope_qkv(const attn_plan *p, const void *q, int64_t qs, const void *
   if (p->p.rope == ATTN_ROPE_NONE) return ATTN_E_INVALID;
   if (!p->ws) return ATTN_E_WORKSPACE;
   const int64_t row = (int64_t)p->p.H * p->p.d;
+  const int64_t kv_row = (int64_t)p->p.Hkv * p->p.d;
   if (p->p.N == 0) return ATTN_OK;
   if (!q || !k || !q_out || !k_out || (v_out && !v)) return ATTN_E_INVALID;
-  if (qs < row || ks < row || (v_out && vs < row)) return ATTN_E_INVALID;
+  if (qs < row || ks < kv_row || (v_out && vs < kv_row)) return ATTN_E_INVALID;
   const int64_t vec = p->p.dtype == ATTN_BF16 ? 8 : 4;
   if (qs % vec || ks % vec || (v_out && vs % vec)) return ATTN_E_ALIGN;
   if (!aligned16(q) || !aligned16(k) || !aligned16(q_out) || !aligned16(k_out) ||
       (v_out && (!aligned16(v) || !aligned16(v_out))))
     return ATTN_E_ALIGN;
-  if ((q_out == q && qs != row) || (k_out == k && ks != row)) return ATTN_E_INVALID;
+  if ((q_out == q && qs != row) || (k_out == k && ks != kv_row)) return ATTN_E_INVALID;
   // the adjacent pairing permutes heads on store: V must be copied with them,
   // and an in-place store would overwrite heads not yet read
   if (p->p.paired == ATTN_PAIRED_ADJACENT && (!v_out || q_out == q || k_out == k))

@@ -119,7 +119,7 @@ template <typename T, int D, bool HALF, int PM>
 __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
     const T *q, int64_t qs, const T *k, int64_t ks, const T *__restrict__ v, int64_t vs, T *qo,
     T *ko, T *__restrict__ vo, const int32_t *__restrict__ tok_pos,
-    const float *__restrict__ tcos, const float *__restrict__ tsin, int64_t N, int H) {
+    const float *__restrict__ tcos, const float *__restrict__ tsin, int64_t N, int H, int Hk) {
   using RC = RopeChunk<T, D, HALF>;
   constexpr int V = RC::V, U = RC::U, NP = RC::NP;
   const int64_t gid = (int64_t)blockIdx.x * kRopeThreads + threadIdx.x;
@@ -138,55 +138,85 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
       sn[par][i] = sr[RC::col(c, i)];
     }
   }
-  const int64_t row = (int64_t)H * D;
   const uint4 *q4 = reinterpret_cast<const uint4 *>(q + n * qs);
   const uint4 *k4 = reinterpret_cast<const uint4 *>(k + n * ks);
-  uint4 *qo4 = reinterpret_cast<uint4 *>(qo + n * row);
-  uint4 *ko4 = reinterpret_cast<uint4 *>(ko + n * row);
+  uint4 *qo4 = reinterpret_cast<uint4 *>(qo + n * (int64_t)H * D);
+  uint4 *ko4 = reinterpret_cast<uint4 *>(ko + n * (int64_t)Hk * D);
   // output position of head hh inside the token's row
   auto out_head = [H](int hh) { return PM == 2 ? (hh & 1) * (H / 2) + hh / 2 : hh; };
-  int h = 0;
-  // two heads per step: eight 16-byte loads in flight before any store
-  for (; h + 1 < H; h += 2) {
-    uint4 in[2][2][2];  // [head][q/k][unit]
+  if (Hk == H) {
+    int h = 0;
+    // two heads per step: eight 16-byte loads in flight before any store
+    for (; h + 1 < H; h += 2) {
+      uint4 in[2][2][2];  // [head][q/k][unit]
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int base = (h + e) * U;
-      in[e][0][0] = q4[base + c];
-      in[e][0][1] = q4[base + c + U / 2];
-      in[e][1][0] = k4[base + c];
-      in[e][1][1] = k4[base + c + U / 2];
+      for (int e = 0; e < 2; ++e) {
+        const int base = (h + e) * U;
+        in[e][0][0] = q4[base + c];
+        in[e][0][1] = q4[base + c + U / 2];
+        in[e][1][0] = k4[base + c];
+        in[e][1][1] = k4[base + c + U / 2];
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int par = PM ? ((h + e) & 1) : 0;
+        const int base = out_head(h + e) * U;
+        uint4 r0, r1;
+        RC::rotate(in[e][0][0], in[e][0][1], cs[par], sn[par], r0, r1);
+        qo4[base + c] = r0;
+        qo4[base + c + U / 2] = r1;
+        RC::rotate(in[e][1][0], in[e][1][1], cs[par], sn[par], r0, r1);
+        ko4[base + c] = r0;
+        ko4[base + c + U / 2] = r1;
+      }
     }
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int par = PM ? ((h + e) & 1) : 0;
-      const int base = out_head(h + e) * U;
+    if (h < H) {  // odd H: unpaired only
+      const int par = PM ? (h & 1) : 0;
+      const int base = h * U;
+      const uint4 a0 = q4[base + c], a1 = q4[base + c + U / 2];
+      const uint4 b0 = k4[base + c], b1 = k4[base + c + U / 2];
       uint4 r0, r1;
-      RC::rotate(in[e][0][0], in[e][0][1], cs[par], sn[par], r0, r1);
+      RC::rotate(a0, a1, cs[par], sn[par], r0, r1);
       qo4[base + c] = r0;
       qo4[base + c + U / 2] = r1;
-      RC::rotate(in[e][1][0], in[e][1][1], cs[par], sn[par], r0, r1);
+      RC::rotate(b0, b1, cs[par], sn[par], r0, r1);
       ko4[base + c] = r0;
       ko4[base + c + U / 2] = r1;
     }
-  }
-  if (h < H) {  // odd H: unpaired only
-    const int par = PM ? (h & 1) : 0;
-    const int base = h * U;
-    const uint4 a0 = q4[base + c], a1 = q4[base + c + U / 2];
-    const uint4 b0 = k4[base + c], b1 = k4[base + c + U / 2];
-    uint4 r0, r1;
-    RC::rotate(a0, a1, cs[par], sn[par], r0, r1);
-    qo4[base + c] = r0;
-    qo4[base + c + U / 2] = r1;
-    RC::rotate(b0, b1, cs[par], sn[par], r0, r1);
-    ko4[base + c] = r0;
-    ko4[base + c + U / 2] = r1;
+  } else {
+    // grouped K/V heads (unpaired): the H query heads, then the Hk key heads,
+    // two heads (four 16-byte loads) per step
+    auto rotate_heads = [&](const uint4 *src, uint4 *dst, int nh) {
+      int h = 0;
+      for (; h + 1 < nh; h += 2) {
+        uint4 in[2][2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          in[e][0] = src[(h + e) * U + c];
+          in[e][1] = src[(h + e) * U + c + U / 2];
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          uint4 r0, r1;
+          RC::rotate(in[e][0], in[e][1], cs[0], sn[0], r0, r1);
+          dst[(h + e) * U + c] = r0;
+          dst[(h + e) * U + c + U / 2] = r1;
+        }
+      }
+      if (h < nh) {
+        uint4 r0, r1;
+        RC::rotate(src[h * U + c], src[h * U + c + U / 2], cs[0], sn[0], r0, r1);
+        dst[h * U + c] = r0;
+        dst[h * U + c + U / 2] = r1;
+      }
+    };
+    rotate_heads(q4, qo4, H);
+    rotate_heads(k4, ko4, Hk);
   }
   if (vo) {
     const uint4 *v4 = reinterpret_cast<const uint4 *>(v + n * vs);
-    uint4 *vo4 = reinterpret_cast<uint4 *>(vo + n * row);
-    for (int hh = 0; hh < H; ++hh) {
+    uint4 *vo4 = reinterpret_cast<uint4 *>(vo + n * (int64_t)Hk * D);
+    for (int hh = 0; hh < Hk; ++hh) {
       const int ob = out_head(hh) * U;
       vo4[ob + c] = v4[hh * U + c];
       vo4[ob + c + U / 2] = v4[hh * U + c + U / 2];
@@ -215,7 +245,7 @@ hipError_t launch_typed(const attn_plan *p, const void *q, int64_t qs, const voi
   const int pm = p->p.paired;
 #define ROPE_LAUNCH(HF, PMV)                                                                   \
   hipLaunchKernelGGL((rope_kernel<T, D, HF, PMV>), grid, dim3(kRopeThreads), 0, stream, Q, qs, K, \
-                     ks, Vv, vs, QO, KO, VO, pos, tc, ts, N, p->p.H)
+                     ks, Vv, vs, QO, KO, VO, pos, tc, ts, N, p->p.H, p->p.Hkv)
   if (half) {
     if (pm == 0) ROPE_LAUNCH(true, 0);
     else if (pm == 1) ROPE_LAUNCH(true, 1);

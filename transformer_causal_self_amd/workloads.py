@@ -34,6 +34,7 @@ class Workload:
     head_dim: int
     rope: int
     paired: int = 0
+    kv_heads: int = 0             # K/V heads (grouped-query); 0 -> heads
     causal: int = 1
     window: int = 0               # key slots, self included; <= 0: none
     scale: float = 0.0            # 0 -> 1/sqrt(head_dim)
@@ -89,15 +90,18 @@ def cu_seqlens(w: Workload, seed: Optional[int] = None) -> np.ndarray:
 
 
 def tensors(w: Workload, seed: Optional[int] = None, with_grad: Optional[bool] = None):
-    """Q, K, V (and dO) as CPU tensors [N, H, d] in the workload's dtype."""
+    """Q, K, V (and dO) as CPU tensors [N, H, d] (K, V: [N, Hkv, d] when grouped)
+    in the workload's dtype."""
     seed = w.num if seed is None else seed
     with_grad = w.backward if with_grad is None else with_grad
     g = torch.Generator().manual_seed(seed)
     shape = (w.n_tokens, w.heads, w.head_dim)
+    kv_shape = (w.n_tokens, w.kv_heads or w.heads, w.head_dim)
     names = ["q", "k", "v"] + (["do"] if with_grad else [])
     out = {}
     for n in names:
-        out[n] = torch.randn(shape, generator=g, dtype=torch.float32).to(w.torch_dtype)
+        out[n] = torch.randn(kv_shape if n in ("k", "v") else shape, generator=g,
+                             dtype=torch.float32).to(w.torch_dtype)
     return out
 
 
