@@ -43,8 +43,12 @@ def _load():
     lib.oracle_attn_bwd.argtypes = [_D, _D, _D, _D] + common + [_D, _D, _D]
     lib.oracle_attn_bwd_sampled.argtypes = ([_D, _D, _D, _D] + common +
                                             [ctypes.c_int64, _I64, _D, ctypes.c_int64, _I64, _D, _D])
+    lib.oracle_rope_bwd.argtypes = lib.oracle_rope.argtypes
+    lib.oracle_rms_norm.argtypes = [_D, ctypes.c_int64, ctypes.c_int, ctypes.c_double, _D]
+    lib.oracle_rms_norm_bwd.argtypes = [_D, _D, ctypes.c_int64, ctypes.c_int, ctypes.c_double, _D]
     for f in (lib.oracle_rope, lib.oracle_attn_fwd, lib.oracle_attn_fwd_rows,
-              lib.oracle_attn_bwd, lib.oracle_attn_bwd_sampled):
+              lib.oracle_attn_bwd, lib.oracle_attn_bwd_sampled, lib.oracle_rope_bwd,
+              lib.oracle_rms_norm, lib.oracle_rms_norm_bwd):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -84,6 +88,49 @@ def rope(x, cu, convention: int, base: float = 10000.0, paired: int = 0):
     _check(_load().oracle_rope(_p(x), N, H, d, _p(cu, _I32), len(cu) - 1, convention, base,
                                paired, _p(y)), "oracle_rope")
     return y
+
+
+def rope_bwd(dy, cu, convention: int, base: float = 10000.0, paired: int = 0):
+    """Transpose of rope: rotation by -phi at the same positions."""
+    dy = _f64(dy)
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    N, H, d = dy.shape
+    dx = np.empty_like(dy)
+    _check(_load().oracle_rope_bwd(_p(dy), N, H, d, _p(cu, _I32), len(cu) - 1, convention, base,
+                                   paired, _p(dx)), "oracle_rope_bwd")
+    return dx
+
+
+def rms_norm(x, eps: float = 1e-6):
+    """x / sqrt(mean(x^2) + eps) over the last axis (no gain)."""
+    x = _f64(x)
+    y = np.empty_like(x)
+    d = x.shape[-1]
+    _check(_load().oracle_rms_norm(_p(x), x.size // d, d, eps, _p(y)), "oracle_rms_norm")
+    return y
+
+
+def rms_norm_bwd(x, dy, eps: float = 1e-6):
+    """Gradient of rms_norm with respect to x."""
+    x, dy = _f64(x), _f64(dy)
+    dx = np.empty_like(x)
+    d = x.shape[-1]
+    _check(_load().oracle_rms_norm_bwd(_p(x), _p(dy), x.size // d, d, eps, _p(dx)),
+           "oracle_rms_norm_bwd")
+    return dx
+
+
+def qk_prep(x, cu, convention: int, base: float = 10000.0, paired: int = 0, norm: bool = False,
+            eps: float = 1e-6):
+    """What rope_qkv makes of Q or K: the RMS-norm (when enabled), then RoPE."""
+    return rope(rms_norm(x, eps) if norm else x, cu, convention, base, paired)
+
+
+def qk_prep_bwd(x, dy, cu, convention: int, base: float = 10000.0, paired: int = 0,
+                norm: bool = False, eps: float = 1e-6):
+    """Gradient of qk_prep with respect to x, given the gradient dy of its output."""
+    g = rope_bwd(dy, cu, convention, base, paired)
+    return rms_norm_bwd(x, g, eps) if norm else g
 
 
 def _heads(H, N, paired):

@@ -32,6 +32,11 @@
  *    head, i.e. key slot j is visible from query slot i iff 0 <= i - j < W.
  *  - Backward: the gradient of L = sum(O * dO) through softmax(s Q K^T) V,
  *    written from the chain rule (the softmax Jacobian is diag(P) - P P^T).
+ *  - QK RMS-norm before the rotation: "Paired Head Attention" article,
+ *    section "Source 4: Triton kernel interleave indexing" (the RoPE kernel
+ *    also applies the Q/K RMS-norm, and its backward uses the same index map);
+ *    the norm itself: "Upgrading a textbook decoder", section 1 "RMSNorm",
+ *    x / sqrt(mean(x^2) + eps) with eps = 1e-6.
  *
  * Conventions: tensors are row-major [N, H, d] (token, head, feature).
  * paired = 0: slot = token, attention head = h.
@@ -138,6 +143,86 @@ int oracle_rope(const double *x, int64_t N, int H, int d, const int32_t *cu, int
         }
       }
     }
+  }
+  return OR_OK;
+}
+
+/*
+ * Transpose of oracle_rope: every pair rotated by -phi at the same positions
+ * (a rotation matrix is orthogonal, its transpose is its inverse):
+ * (a, b) -> (a cos + b sin, b cos - a sin).  This carries a gradient with
+ * respect to the rotated values back to the values before the rotation.
+ */
+int oracle_rope_bwd(const double *dy, int64_t N, int H, int d, const int32_t *cu, int S,
+                    int convention, double base, int paired, double *dx) {
+  if (!dy || !dx || !check_shape(N, H, d, paired) || !check_cu(cu, S, N)) return OR_EINVAL;
+  if (convention != 1 && convention != 2) return OR_EINVAL;
+  if (d % 2) return OR_EINVAL;
+  if (!(base > 0.0)) return OR_EINVAL;
+  const int half = d / 2;
+  for (int k = 0; k < S; ++k) {
+    const int64_t start = cu[k], end = cu[k + 1];
+#pragma omp parallel for schedule(static)
+    for (int64_t n = start; n < end; ++n) {
+      const int64_t t = n - start;
+      for (int h = 0; h < H; ++h) {
+        const double *yr = dy + (n * H + h) * (int64_t)d;
+        double *xr = dx + (n * H + h) * (int64_t)d;
+        const double p = (double)rope_position(t, h, paired);
+        for (int i = 0; i < half; ++i) {
+          const double phi = p * pow(base, -2.0 * (double)i / (double)d);
+          const double c = cos(phi), s = sin(phi);
+          const int ia = (convention == 1) ? i : 2 * i;
+          const int ib = (convention == 1) ? i + half : 2 * i + 1;
+          const double a = yr[ia], b = yr[ib];
+          xr[ia] = a * c + b * s;
+          xr[ib] = b * c - a * s;
+        }
+      }
+    }
+  }
+  return OR_OK;
+}
+
+/*
+ * RMS normalisation of each of `rows` rows of d values ("Upgrading a textbook
+ * decoder", section 1 "RMSNorm"): y = x / sqrt(mean(x^2) + eps), without a
+ * gain (a gain of ones).
+ */
+int oracle_rms_norm(const double *x, int64_t rows, int d, double eps, double *y) {
+  if (!x || !y || rows < 0 || d <= 0 || !(eps >= 0.0)) return OR_EINVAL;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const double *xr = x + r * d;
+    double ms = 0.0;
+    for (int i = 0; i < d; ++i) ms += xr[i] * xr[i];
+    ms /= d;
+    const double inv = 1.0 / sqrt(ms + eps);
+    for (int i = 0; i < d; ++i) y[r * d + i] = xr[i] * inv;
+  }
+  return OR_OK;
+}
+
+/*
+ * Gradient of oracle_rms_norm.  With r = 1 / sqrt(mean(x^2) + eps), y_i = x_i r
+ * and dr/dx_j = -r^3 x_j / d, so the chain rule gives
+ *     dx_j = r dy_j - (r^3 / d) x_j sum_i dy_i x_i.
+ */
+int oracle_rms_norm_bwd(const double *x, const double *dy, int64_t rows, int d, double eps,
+                        double *dx) {
+  if (!x || !dy || !dx || rows < 0 || d <= 0 || !(eps >= 0.0)) return OR_EINVAL;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const double *xr = x + r * d, *gr = dy + r * d;
+    double ms = 0.0, xg = 0.0;
+    for (int i = 0; i < d; ++i) {
+      ms += xr[i] * xr[i];
+      xg += xr[i] * gr[i];
+    }
+    ms /= d;
+    const double inv = 1.0 / sqrt(ms + eps);
+    const double c = inv * inv * inv / d * xg;
+    for (int i = 0; i < d; ++i) dx[r * d + i] = inv * gr[i] - c * xr[i];
   }
   return OR_OK;
 }
