@@ -1,7 +1,7 @@
 """Benchmark of the rotary causal self-attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--paired P]
-                    [--kv-heads G] [--no-cpu-baseline]
+                    [--kv-heads G] [--qk-norm] [--rope-bwd] [--no-cpu-baseline]
 
 One step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: rope_qkv (Q, K rotated), attn_fwd (O, LSE) and, for
@@ -46,6 +46,10 @@ def parse():
                          "where rope_qkv also copies V in the slot layout)")
     ap.add_argument("--kv-heads", type=int, default=None,
                     help="grouped-query attention: number of K/V heads (divides the heads)")
+    ap.add_argument("--qk-norm", action="store_true",
+                    help="RMS-normalise Q and K rows inside rope_qkv")
+    ap.add_argument("--rope-bwd", action="store_true",
+                    help="add rope_qkv_bwd (gradients back to the raw Q, K) to a backward step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -76,7 +80,7 @@ def stored_traffic(kernel, workload, digest):
     return r.get("bytes_per_launch")
 
 
-def cpu_baseline(w, inp, seconds):
+def cpu_baseline(w, inp, seconds, norm=False):
     """fp64 oracle on a bounded random sample of the forward's query rows (plus
     its RoPE of every token), scaled to causal TFLOP/s."""
     import numpy as np
@@ -107,8 +111,8 @@ def cpu_baseline(w, inp, seconds):
 
     # calibrate: the RoPE of every token is a fixed cost, rows scale linearly
     t0 = time.perf_counter()
-    qr = oracle.rope(q, cu, w.rope, w.rope_base, w.paired)
-    kr = oracle.rope(k, cu, w.rope, w.rope_base, w.paired)
+    qr = oracle.qk_prep(q, cu, w.rope, w.rope_base, w.paired, norm)
+    kr = oracle.qk_prep(k, cu, w.rope, w.rope_base, w.paired, norm)
     t_rope = time.perf_counter() - t0
     # each call has a fixed gather cost plus a per-row cost: two probe sizes
     t_probe = []
@@ -122,8 +126,8 @@ def cpu_baseline(w, inp, seconds):
 
     rows = rows_sample(n)
     t0 = time.perf_counter()
-    qr = oracle.rope(q, cu, w.rope, w.rope_base, w.paired)
-    kr = oracle.rope(k, cu, w.rope, w.rope_base, w.paired)
+    qr = oracle.qk_prep(q, cu, w.rope, w.rope_base, w.paired, norm)
+    kr = oracle.qk_prep(k, cu, w.rope, w.rope_base, w.paired, norm)
     fwd_rows(qr, kr, rows)
     dt = time.perf_counter() - t0
     flops = sum(4.0 * w.head_dim * visible(int(s)) for s in rows[:, 1])
@@ -159,7 +163,7 @@ def main():
                                 "fp32" if w.dtype == wl.DTYPE_FP32 else "bf16", inp["cu"],
                                 causal=w.causal, window=w.window, softmax_scale=w.scale,
                                 rope=w.rope, rope_base=w.rope_base, paired=w.paired,
-                                num_kv_heads=w.kv_heads).bind(dev)
+                                num_kv_heads=w.kv_heads, qk_norm=int(args.qk_norm)).bind(dev)
     info = plan.info
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
     do = inp["do"].to(dev) if w.backward else None
@@ -185,7 +189,13 @@ def main():
                 raise
             grads = None        # backward kernels not built into this library
 
-    names = ["rope_qkv", "attn_fwd"] + (["attn_bwd"] if grads is not None else [])
+    rope_bwd = args.rope_bwd and grads is not None
+    if rope_bwd:
+        raw_grads = (torch.empty_like(grads[0]), torch.empty_like(grads[1]))
+        tca.rope_qkv_bwd(plan, grads[0], grads[1], q, k, dq_out=raw_grads[0],
+                         dk_out=raw_grads[1])
+    names = ["rope_qkv", "attn_fwd"] + (["attn_bwd"] if grads is not None else []) + (
+        ["rope_qkv_bwd"] if rope_bwd else [])
     events = {n: [] for n in names}
 
     def step(record):
@@ -203,6 +213,10 @@ def main():
         timed("attn_fwd", lambda: tca.attn_fwd(plan, q2, k2, v2, o, lse))
         if grads is not None:
             timed("attn_bwd", lambda: tca.attn_bwd(plan, q2, k2, v2, o, lse, do, *grads))
+        if rope_bwd:
+            timed("rope_qkv_bwd", lambda: tca.rope_qkv_bwd(plan, grads[0], grads[1], q, k,
+                                                            dq_out=raw_grads[0],
+                                                            dk_out=raw_grads[1]))
 
     for _ in range(args.warmup):
         step(False)
@@ -224,16 +238,21 @@ def main():
     kern_ms = {n: sum(a.elapsed_time(b) for a, b in events[n]) / len(events[n]) for n in names}
     digest = kernel_sources_digest()
     wname = f"problem{w.num}" + ("" if args.paired is None else f"-paired{w.paired}") + (
-        "" if args.kv_heads is None else f"-kv{w.kv_heads}")
+        "" if args.kv_heads is None else f"-kv{w.kv_heads}") + ("-qknorm" if args.qk_norm else "")
     # rope_qkv algorithmic bytes: Q, K read and written (plus V when copied)
     rope_bytes = info["rope_bytes"] * (1.5 if copy_v else 1.0)
+    # rope_qkv_bwd: fp32 gradients of Q', K' read and of Q, K written, plus the
+    # raw Q, K read again for the norm's gradient
+    qk_elems = info["rope_bytes"] / 2 / (2 if w.dtype == wl.DTYPE_BF16 else 4)
+    rope_bwd_bytes = qk_elems * (8 + ((2 if w.dtype == wl.DTYPE_BF16 else 4) if args.qk_norm
+                                      else 0))
     step_flops = info["fwd_flops"] + (info["bwd_flops"] if grads is not None else 0.0)
     kernels = {}
     peak_mm = PEAK_BF16_TFLOPS if w.dtype == wl.DTYPE_BF16 else PEAK_FP32_TFLOPS
     for n in names:
         t = kern_ms[n] * 1e-3
-        if n == "rope_qkv":
-            ach = rope_bytes / t / 1e9
+        if n in ("rope_qkv", "rope_qkv_bwd"):
+            ach = (rope_bytes if n == "rope_qkv" else rope_bwd_bytes) / t / 1e9
             rl = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                   "frac": ach / PEAK_HBM_GBS}
         else:
@@ -265,6 +284,7 @@ def main():
                    "head_dim": w.head_dim, "sequences": len(inp["cu"]) - 1,
                    "window": w.window, "paired": w.paired, "v_copied_by_rope": copy_v,
                    "kv_heads": w.kv_heads or w.heads,
+                   "qk_norm": bool(args.qk_norm),
                    "rope": {1: "half-split", 2: "adjacent"}.get(w.rope, "none"),
                    "step": "+".join(names), "parallelism": "single GPU"},
         "roofline": roof,
@@ -277,7 +297,7 @@ def main():
         "kernel_sources": digest,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds, args.qk_norm)
     print(json.dumps(out), flush=True)
 
 

@@ -105,6 +105,10 @@ typedef struct {
   int32_t num_kv_heads;      /* Hkv: 0 or H for one K/V head per query head; else a
                                 divisor of H (grouped-query attention, unpaired
                                 only: ATTN_E_UNSUPPORTED with pairing) */
+  int32_t qk_norm;           /* 0: none; 1: rope_qkv first RMS-normalises every Q and
+                                K head row over d, x / sqrt(mean(x^2) + eps), in
+                                fp32 and without a gain */
+  float norm_eps;            /* eps of that norm; 0 selects 1e-6 */
 } attn_problem;
 
 /* Counts for throughput and roofline reporting (exact, from the plan). */
@@ -185,6 +189,11 @@ attn_status attn_plan_work_items(const attn_plan *plan, int32_t which, int32_t *
  * ATTN_PAIRED_ADJACENT: the outputs are written in that layout's head order
  * (see Layouts), so v_out is required (V' feeds attn_fwd) and neither output
  * may alias its input (ATTN_E_INVALID otherwise).
+ * QK norm ("Paired Head Attention", section "Source 4: Triton kernel
+ * interleave indexing": the rotary kernel also applies the Q/K RMS-norm;
+ * "Upgrading a textbook decoder", section 1 "RMSNorm"): when the plan sets
+ * qk_norm, each head row of Q and K is divided by sqrt(mean(x^2) + eps)
+ * before it is rotated, in the same pass.
  * The plan's rope mode must not be ATTN_ROPE_NONE (ATTN_E_INVALID).
  */
 attn_status rope_qkv(const attn_plan *plan, const void *q, int64_t q_tok_stride, const void *k,
@@ -219,6 +228,29 @@ attn_status attn_fwd(const attn_plan *plan, const void *q, const void *k, const 
 attn_status attn_bwd(const attn_plan *plan, const void *q, const void *k, const void *v,
                      const void *o, const float *lse, const void *d_o, float *dq, float *dk,
                      float *dv, void *stream);
+
+/*
+ * Backward of rope_qkv: the gradients with respect to its inputs q, k (before
+ * the norm and the rotation), given the gradients d_q, d_k of its outputs
+ * Q', K' as attn_bwd writes them.  Per head row: rotation by -phi at the same
+ * positions (the transpose of the rotation; same paired stagger), then, when
+ * the plan sets qk_norm, the norm's gradient
+ *     dx = r g - (r^3 / d) x (g . x),   r = 1 / sqrt(mean(x^2) + eps),
+ * which needs the forward inputs q, k (plan dtype, token strides as in
+ * rope_qkv; ignored and may be NULL without qk_norm).
+ * d_q: float [N', H', d] slot layout (= [N, H, d] memory), d_k: likewise with
+ * Hkv heads; dq_out, dk_out: float [N, H, d] / [N, Hkv, d] in head order.
+ * d_v / dv_out (optional, both or neither): dV copied from the slot layout
+ * into head order (V is not rotated; this only matters for the adjacent
+ * pairing, whose slot layout permutes heads).
+ * Outputs may alias d_q / d_k / d_v except with ATTN_PAIRED_ADJACENT
+ * (ATTN_E_INVALID).  Floats 16-byte aligned; token strides of q, k multiples
+ * of 8 (bf16) or 4 (fp32) elements.
+ */
+attn_status rope_qkv_bwd(const attn_plan *plan, const void *q, int64_t q_tok_stride,
+                         const void *k, int64_t k_tok_stride, const float *d_q, const float *d_k,
+                         const float *d_v, float *dq_out, float *dk_out, float *dv_out,
+                         void *stream);
 
 /* Static description of a status code. */
 const char *attn_status_str(attn_status status);

@@ -24,7 +24,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = set(declared_functions())
     assert {"attn_plan_create", "attn_plan_workspace_bytes", "attn_plan_bind", "attn_plan_stats",
-            "attn_plan_work_items", "rope_qkv", "attn_fwd", "attn_bwd", "attn_status_str",
+            "attn_plan_work_items", "rope_qkv", "rope_qkv_bwd", "attn_fwd", "attn_bwd",
+            "attn_status_str",
             "attn_plan_destroy"} <= names
 
 
@@ -65,6 +66,9 @@ def plan(**kw):
     (dict(num_heads=6, num_kv_heads=4), -1),           # K/V heads must divide H
     (dict(num_heads=6, num_kv_heads=-1), -1),
     (dict(num_heads=6, num_kv_heads=3, paired=1), -2), # grouped K/V heads are unpaired only
+    (dict(qk_norm=2), -1),
+    (dict(qk_norm=1, rope=0), -1),                     # the norm runs inside rope_qkv
+    (dict(qk_norm=1, norm_eps=-1e-6), -1),
     (dict(head_dim=32), -2),                           # valid, not covered by the kernels
     (dict(head_dim=96), -2),
 ])

@@ -48,7 +48,8 @@ class _Problem(ctypes.Structure):
                 ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("rope", ctypes.c_int32),
                 ("rope_base", ctypes.c_double), ("paired", ctypes.c_int32),
-                ("num_kv_heads", ctypes.c_int32)]
+                ("num_kv_heads", ctypes.c_int32), ("qk_norm", ctypes.c_int32),
+                ("norm_eps", ctypes.c_float)]
 
 
 class _Info(ctypes.Structure):
@@ -84,6 +85,7 @@ def load_library():
     lib.attn_plan_stats.argtypes = [vp, ctypes.POINTER(_Info)]
     lib.attn_plan_work_items.argtypes = [vp, i32, ctypes.POINTER(i32), i64, ctypes.POINTER(i64)]
     lib.rope_qkv.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, vp, vp, vp]
+    lib.rope_qkv_bwd.argtypes = [vp, vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp]
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.attn_status_str.argtypes = [ctypes.c_int]
@@ -91,7 +93,7 @@ def load_library():
     lib.attn_plan_destroy.argtypes = [vp]
     lib.attn_plan_destroy.restype = None
     for f in ("attn_plan_create", "attn_plan_bind", "attn_plan_stats", "attn_plan_work_items",
-              "rope_qkv", "attn_fwd", "attn_bwd"):
+              "rope_qkv", "rope_qkv_bwd", "attn_fwd", "attn_bwd"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -165,7 +167,7 @@ class Plan:
 def attn_plan_create(num_tokens: int, num_heads: int, head_dim: int, dtype, cu_seqlens,
                      causal: int = 1, window: int = 0, softmax_scale: float = 0.0, rope="half",
                      rope_base: float = 10000.0, paired: int = 0,
-                     num_kv_heads: int = 0) -> Plan:
+                     num_kv_heads: int = 0, qk_norm: int = 0, norm_eps: float = 0.0) -> Plan:
     if isinstance(dtype, str):
         dtype = {"bf16": ATTN_BF16, "fp32": ATTN_FP32}[dtype]
     elif isinstance(dtype, torch.dtype):
@@ -175,13 +177,14 @@ def attn_plan_create(num_tokens: int, num_heads: int, head_dim: int, dtype, cu_s
                   cu_seqlens=cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                   num_seqs=len(cu) - 1, causal=causal, window=window,
                   softmax_scale=softmax_scale, rope=ROPE.get(rope, rope), rope_base=rope_base,
-                  paired=paired, num_kv_heads=num_kv_heads)
+                  paired=paired, num_kv_heads=num_kv_heads, qk_norm=qk_norm, norm_eps=norm_eps)
     h = ctypes.c_void_p()
     _check("attn_plan_create", load_library().attn_plan_create(ctypes.byref(pr), ctypes.byref(h)))
     problem = dict(num_tokens=num_tokens, num_heads=num_heads, head_dim=head_dim, dtype=dtype,
                    cu_seqlens=cu.copy(), causal=causal, window=window,
                    softmax_scale=softmax_scale, rope=ROPE.get(rope, rope), rope_base=rope_base,
-                   paired=paired, num_kv_heads=num_kv_heads or num_heads)
+                   paired=paired, num_kv_heads=num_kv_heads or num_heads, qk_norm=qk_norm,
+                   norm_eps=norm_eps)
     return Plan(h.value, problem)
 
 
@@ -225,6 +228,39 @@ def rope_qkv(plan: Plan, q, k, v=None, q_out=None, k_out=None, v_out=None):
         v.data_ptr() if v_out is not None else None, vs, q_out.data_ptr(), k_out.data_ptr(),
         v_out.data_ptr() if v_out is not None else None, _stream(q.device)))
     return (q_out, k_out) if v_out is None else (q_out, k_out, v_out)
+
+
+def rope_qkv_bwd(plan: Plan, d_q, d_k, q=None, k=None, d_v=None, dq_out=None, dk_out=None,
+                 dv_out=None):
+    """Gradients with respect to rope_qkv's inputs (before the QK norm and the
+    rotation), given float32 gradients of its outputs in the slot layout.
+    q, k (the forward inputs) are needed when the plan normalises.  Returns
+    (dq, dk[, dv]) float32 in head order."""
+    p = plan.problem
+    H, Hkv, d = p["num_heads"], p["num_kv_heads"], p["head_dim"]
+    _need(plan, d_q, "d_q", torch.float32)
+    _need(plan, d_k, "d_k", torch.float32, kv=True)
+    if d_v is not None:
+        _need(plan, d_v, "d_v", torch.float32, kv=True)
+    dq_out = torch.empty_like(d_q) if dq_out is None else dq_out
+    dk_out = torch.empty_like(d_k) if dk_out is None else dk_out
+    if d_v is not None and dv_out is None:
+        dv_out = torch.empty_like(d_v)
+    _need(plan, dq_out, "dq_out", torch.float32)
+    _need(plan, dk_out, "dk_out", torch.float32, kv=True)
+    qs = ks = 0
+    if p["qk_norm"]:
+        if q is None or k is None:
+            raise ValueError("the QK norm's backward needs the forward inputs q and k")
+        _need(plan, q, "q", dense=False)
+        _need(plan, k, "k", dense=False)
+        qs, ks = _token_stride(q, H, d), _token_stride(k, Hkv, d)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    _check("rope_qkv_bwd", load_library().rope_qkv_bwd(
+        plan.handle, ptr(q) if p["qk_norm"] else None, qs, ptr(k) if p["qk_norm"] else None, ks,
+        d_q.data_ptr(), d_k.data_ptr(), ptr(d_v), dq_out.data_ptr(), dk_out.data_ptr(),
+        ptr(dv_out) if d_v is not None else None, _stream(d_q.device)))
+    return (dq_out, dk_out) if d_v is None else (dq_out, dk_out, dv_out)
 
 
 def attn_fwd(plan: Plan, q, k, v, o=None, lse=None):

@@ -61,6 +61,8 @@ struct Problem {
   int32_t Hkv;     // K/V heads given (= H unless grouped)
   int32_t Hks;     // K/V attention heads (= Hs unless grouped)
   int32_t G;       // query heads per K/V head: Hs / Hks
+  int32_t qk_norm; // RMS-norm of Q and K rows before the rotation
+  float norm_eps;
 };
 
 }  // namespace attn

@@ -157,6 +157,9 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
     return ATTN_E_INVALID;
   if (pr->paired && (pr->num_heads % 2)) return ATTN_E_INVALID;
   if (!std::isfinite(pr->softmax_scale) || pr->softmax_scale < 0.0f) return ATTN_E_INVALID;
+  if (pr->qk_norm != 0 && pr->qk_norm != 1) return ATTN_E_INVALID;
+  if (pr->qk_norm && pr->rope == ATTN_ROPE_NONE) return ATTN_E_INVALID;  // applied by rope_qkv
+  if (!std::isfinite(pr->norm_eps) || pr->norm_eps < 0.0f) return ATTN_E_INVALID;
   if (pr->head_dim <= 0 || (pr->head_dim % 2)) return ATTN_E_INVALID;
   const int mult = pr->paired ? 2 : 1;
   // slots are int32 inside the kernels
@@ -193,6 +196,8 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
     P.Hkv = Hkv;
     P.Hks = pr->paired ? P.Hs : Hkv;
     P.G = P.Hs / P.Hks;
+    P.qk_norm = pr->qk_norm;
+    P.norm_eps = pr->norm_eps == 0.0f ? 1e-6f : pr->norm_eps;
     P.Ns = P.N * mult;
     p->cu.assign(cu, cu + S + 1);
 
@@ -378,6 +383,32 @@ attn_status rope_qkv(const attn_plan *p, const void *q, int64_t qs, const void *
     return ATTN_E_INVALID;
   return attn::launch_rope(p, q, qs, k, ks, v_out ? v : nullptr, vs, q_out, k_out, v_out,
                            static_cast<hipStream_t>(stream));
+}
+
+attn_status rope_qkv_bwd(const attn_plan *p, const void *q, int64_t qs, const void *k,
+                         int64_t ks, const float *d_q, const float *d_k, const float *d_v,
+                         float *dq_out, float *dk_out, float *dv_out, void *stream) {
+  if (!p) return ATTN_E_INVALID;
+  if (p->p.rope == ATTN_ROPE_NONE) return ATTN_E_INVALID;
+  if (!p->ws) return ATTN_E_WORKSPACE;
+  if (p->p.N == 0) return ATTN_OK;
+  if (!d_q || !d_k || !dq_out || !dk_out || (!d_v != !dv_out)) return ATTN_E_INVALID;
+  const void *fl[] = {d_q, d_k, dq_out, dk_out, d_v, dv_out};
+  for (const void *x : fl)
+    if (x && !aligned16(x)) return ATTN_E_ALIGN;
+  if (p->p.paired == ATTN_PAIRED_ADJACENT &&
+      (dq_out == d_q || dk_out == d_k || (dv_out && dv_out == d_v)))
+    return ATTN_E_INVALID;
+  if (p->p.qk_norm) {
+    const int64_t row = (int64_t)p->p.H * p->p.d, kv_row = (int64_t)p->p.Hkv * p->p.d;
+    if (!q || !k) return ATTN_E_INVALID;
+    if (qs < row || ks < kv_row) return ATTN_E_INVALID;
+    const int64_t vec = p->p.dtype == ATTN_BF16 ? 8 : 4;
+    if (qs % vec || ks % vec || !aligned16(q) || !aligned16(k)) return ATTN_E_ALIGN;
+  }
+  return attn::launch_rope_bwd(p, p->p.qk_norm ? q : nullptr, qs, p->p.qk_norm ? k : nullptr, ks,
+                               d_q, d_k, d_v, dq_out, dk_out, dv_out,
+                               static_cast<hipStream_t>(stream));
 }
 
 attn_status attn_fwd(const attn_plan *p, const void *q, const void *k, const void *v, void *o,

@@ -20,6 +20,14 @@
 // idea") puts head h at slot 2t + (h mod 2), attention head h / 2, which in the
 // dense [2N, H/2, d] output is position (h mod 2) * H/2 + h / 2 of the token's
 // row: the store permutes heads (V is copied with the same permutation).
+//
+// Grouped K/V heads: K (and V) carry Hkv heads; their rows are rotated after
+// the H query rows.  QK norm ("Paired Head Attention", section "Source 4":
+// the rotary kernel also applies the Q/K RMS-norm; "Upgrading a textbook
+// decoder", section 1 "RMSNorm"): each row is divided by sqrt(mean(x^2) + eps)
+// in fp32 before its rotation; the row's sum of squares is spread over the
+// lanes of its token and summed across them.  The backward kernel at the end
+// of this file rotates gradient rows by -phi and applies the norm's gradient.
 #include "attn_internal.h"
 #include "device_common.h"
 #include "launch.h"
@@ -70,6 +78,14 @@ __device__ __forceinline__ uint4 pack<float>(const float *f) {
                     __float_as_uint(f[3]));
 }
 
+// Sum over each aligned group of L consecutive lanes (the lanes of one token).
+template <int L>
+__device__ __forceinline__ float lanes_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < L; m <<= 1) v += __shfl_xor(v, m, L);
+  return v;
+}
+
 // Work split: a row of D elements is U = D / V sixteen-byte units (V elements
 // each).  Thread (token n, chunk c) owns units c and c + U/2 of every head row of
 // that token, so each load/store instruction of a wave covers whole 128-byte
@@ -87,39 +103,66 @@ struct RopeChunk {
     if (HALF) return c * V + i;
     return (i < V / 2) ? c * (V / 2) + i : (c + U / 2) * (V / 2) + (i - V / 2);
   }
-  __device__ static __forceinline__ void rotate(const uint4 &u0, const uint4 &u1, const float *cs,
-                                                const float *sn, uint4 &r0, uint4 &r1) {
-    float a[V], b[V], x[V], y[V];
-    unpack<T>(u0, a);
-    unpack<T>(u1, b);
+  // rotation of the unpacked pair values a (unit c) and b (unit c + U/2),
+  // each first multiplied by `scale`; packed back to T
+  __device__ static __forceinline__ void rotate_vals(const float *a, const float *b,
+                                                     const float *cs, const float *sn, float scale,
+                                                     uint4 &r0, uint4 &r1) {
+    float x[V], y[V];
     if (HALF) {
 #pragma unroll
       for (int i = 0; i < V; ++i) {
-        x[i] = fmaf(a[i], cs[i], -b[i] * sn[i]);
-        y[i] = fmaf(b[i], cs[i], a[i] * sn[i]);
+        const float ai = a[i] * scale, bi = b[i] * scale;
+        x[i] = fmaf(ai, cs[i], -bi * sn[i]);
+        y[i] = fmaf(bi, cs[i], ai * sn[i]);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < V / 2; ++i) {
-        x[2 * i] = fmaf(a[2 * i], cs[i], -a[2 * i + 1] * sn[i]);
-        x[2 * i + 1] = fmaf(a[2 * i + 1], cs[i], a[2 * i] * sn[i]);
+        const float a0 = a[2 * i] * scale, a1 = a[2 * i + 1] * scale;
+        const float b0 = b[2 * i] * scale, b1 = b[2 * i + 1] * scale;
+        x[2 * i] = fmaf(a0, cs[i], -a1 * sn[i]);
+        x[2 * i + 1] = fmaf(a1, cs[i], a0 * sn[i]);
         const int j = V / 2 + i;
-        y[2 * i] = fmaf(b[2 * i], cs[j], -b[2 * i + 1] * sn[j]);
-        y[2 * i + 1] = fmaf(b[2 * i + 1], cs[j], b[2 * i] * sn[j]);
+        y[2 * i] = fmaf(b0, cs[j], -b1 * sn[j]);
+        y[2 * i + 1] = fmaf(b1, cs[j], b0 * sn[j]);
       }
     }
     r0 = pack<T>(x);
     r1 = pack<T>(y);
   }
+  __device__ static __forceinline__ void rotate(const uint4 &u0, const uint4 &u1, const float *cs,
+                                                const float *sn, uint4 &r0, uint4 &r1) {
+    float a[V], b[V];
+    unpack<T>(u0, a);
+    unpack<T>(u1, b);
+    rotate_vals(a, b, cs, sn, 1.0f, r0, r1);
+  }
+  // RMS-norm then rotation of one head row: the sum of squares over the row is
+  // spread over the U/2 lanes of the token and summed across them
+  __device__ static __forceinline__ void norm_rotate(const uint4 &u0, const uint4 &u1,
+                                                     const float *cs, const float *sn, float eps,
+                                                     uint4 &r0, uint4 &r1) {
+    float a[V], b[V];
+    unpack<T>(u0, a);
+    unpack<T>(u1, b);
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) ss = fmaf(a[i], a[i], fmaf(b[i], b[i], ss));
+    ss = lanes_sum<U / 2>(ss);
+    rotate_vals(a, b, cs, sn, rsqrtf(ss * (1.0f / D) + eps), r0, r1);
+  }
 };
 
 // PM: 0 unpaired, 1 paired (partner h + H/2, no permutation), 2 paired
 // adjacent (partner h ^ 1, heads permuted on store).
-template <typename T, int D, bool HALF, int PM>
+// NORM: RMS-normalise each Q and K head row (eps) before rotating it.
+template <typename T, int D, bool HALF, int PM, bool NORM>
 __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
     const T *q, int64_t qs, const T *k, int64_t ks, const T *__restrict__ v, int64_t vs, T *qo,
     T *ko, T *__restrict__ vo, const int32_t *__restrict__ tok_pos,
-    const float *__restrict__ tcos, const float *__restrict__ tsin, int64_t N, int H, int Hk) {
+    const float *__restrict__ tcos, const float *__restrict__ tsin, int64_t N, int H, int Hk,
+    float eps) {
   using RC = RopeChunk<T, D, HALF>;
   constexpr int V = RC::V, U = RC::U, NP = RC::NP;
   const int64_t gid = (int64_t)blockIdx.x * kRopeThreads + threadIdx.x;
@@ -142,6 +185,13 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
   const uint4 *k4 = reinterpret_cast<const uint4 *>(k + n * ks);
   uint4 *qo4 = reinterpret_cast<uint4 *>(qo + n * (int64_t)H * D);
   uint4 *ko4 = reinterpret_cast<uint4 *>(ko + n * (int64_t)Hk * D);
+  auto rot = [eps](const uint4 &u0, const uint4 &u1, const float *c_, const float *s_, uint4 &r0,
+                   uint4 &r1) {
+    if (NORM)
+      RC::norm_rotate(u0, u1, c_, s_, eps, r0, r1);
+    else
+      RC::rotate(u0, u1, c_, s_, r0, r1);
+  };
   // output position of head hh inside the token's row
   auto out_head = [H](int hh) { return PM == 2 ? (hh & 1) * (H / 2) + hh / 2 : hh; };
   if (Hk == H) {
@@ -162,10 +212,10 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
         const int par = PM ? ((h + e) & 1) : 0;
         const int base = out_head(h + e) * U;
         uint4 r0, r1;
-        RC::rotate(in[e][0][0], in[e][0][1], cs[par], sn[par], r0, r1);
+        rot(in[e][0][0], in[e][0][1], cs[par], sn[par], r0, r1);
         qo4[base + c] = r0;
         qo4[base + c + U / 2] = r1;
-        RC::rotate(in[e][1][0], in[e][1][1], cs[par], sn[par], r0, r1);
+        rot(in[e][1][0], in[e][1][1], cs[par], sn[par], r0, r1);
         ko4[base + c] = r0;
         ko4[base + c + U / 2] = r1;
       }
@@ -176,10 +226,10 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
       const uint4 a0 = q4[base + c], a1 = q4[base + c + U / 2];
       const uint4 b0 = k4[base + c], b1 = k4[base + c + U / 2];
       uint4 r0, r1;
-      RC::rotate(a0, a1, cs[par], sn[par], r0, r1);
+      rot(a0, a1, cs[par], sn[par], r0, r1);
       qo4[base + c] = r0;
       qo4[base + c + U / 2] = r1;
-      RC::rotate(b0, b1, cs[par], sn[par], r0, r1);
+      rot(b0, b1, cs[par], sn[par], r0, r1);
       ko4[base + c] = r0;
       ko4[base + c + U / 2] = r1;
     }
@@ -198,14 +248,14 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           uint4 r0, r1;
-          RC::rotate(in[e][0], in[e][1], cs[0], sn[0], r0, r1);
+          rot(in[e][0], in[e][1], cs[0], sn[0], r0, r1);
           dst[(h + e) * U + c] = r0;
           dst[(h + e) * U + c + U / 2] = r1;
         }
       }
       if (h < nh) {
         uint4 r0, r1;
-        RC::rotate(src[h * U + c], src[h * U + c + U / 2], cs[0], sn[0], r0, r1);
+        rot(src[h * U + c], src[h * U + c + U / 2], cs[0], sn[0], r0, r1);
         dst[h * U + c] = r0;
         dst[h * U + c + U / 2] = r1;
       }
@@ -243,23 +293,184 @@ hipError_t launch_typed(const attn_plan *p, const void *q, int64_t qs, const voi
   T *VO = static_cast<T *>(vo);
   const bool half = p->p.rope == ATTN_ROPE_HALF;
   const int pm = p->p.paired;
-#define ROPE_LAUNCH(HF, PMV)                                                                   \
-  hipLaunchKernelGGL((rope_kernel<T, D, HF, PMV>), grid, dim3(kRopeThreads), 0, stream, Q, qs, K, \
-                     ks, Vv, vs, QO, KO, VO, pos, tc, ts, N, p->p.H, p->p.Hkv)
-  if (half) {
-    if (pm == 0) ROPE_LAUNCH(true, 0);
-    else if (pm == 1) ROPE_LAUNCH(true, 1);
-    else ROPE_LAUNCH(true, 2);
+  const float eps = p->p.norm_eps;
+#define ROPE_LAUNCH(HF, PMV, NRM)                                                          \
+  hipLaunchKernelGGL((rope_kernel<T, D, HF, PMV, NRM>), grid, dim3(kRopeThreads), 0, stream, Q, \
+                     qs, K, ks, Vv, vs, QO, KO, VO, pos, tc, ts, N, p->p.H, p->p.Hkv, eps)
+#define ROPE_PM(HF, NRM)                \
+  do {                                  \
+    if (pm == 0) ROPE_LAUNCH(HF, 0, NRM); \
+    else if (pm == 1) ROPE_LAUNCH(HF, 1, NRM); \
+    else ROPE_LAUNCH(HF, 2, NRM);       \
+  } while (0)
+  if (p->p.qk_norm) {
+    if (half) ROPE_PM(true, true);
+    else ROPE_PM(false, true);
   } else {
-    if (pm == 0) ROPE_LAUNCH(false, 0);
-    else if (pm == 1) ROPE_LAUNCH(false, 1);
-    else ROPE_LAUNCH(false, 2);
+    if (half) ROPE_PM(true, false);
+    else ROPE_PM(false, false);
   }
+#undef ROPE_PM
 #undef ROPE_LAUNCH
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- backward --
+// Backward of rope_qkv for one token per group of D/8 lanes: the incoming
+// gradient rows (fp32, read from the slot layout) are rotated by -phi, the
+// transpose of the forward rotation, and with NORM pushed through the RMS-norm:
+// dx = r g - (r^3 / D) x (g . x), r = 1 / sqrt(mean(x^2) + eps), x the forward
+// input row (plan dtype).  Lane (token n, chunk c) owns the fp32 units c and
+// c + D/8 of every row (4 elements each).
+template <typename T>
+__device__ __forceinline__ void load4(const T *p, float *f);
+template <>
+__device__ __forceinline__ void load4<__bf16>(const __bf16 *p, float *f) {
+  const uint2 u = *reinterpret_cast<const uint2 *>(p);
+  f[0] = bf16_lo(u.x);
+  f[1] = bf16_hi(u.x);
+  f[2] = bf16_lo(u.y);
+  f[3] = bf16_hi(u.y);
+}
+template <>
+__device__ __forceinline__ void load4<float>(const float *p, float *f) {
+  const float4 u = *reinterpret_cast<const float4 *>(p);
+  f[0] = u.x;
+  f[1] = u.y;
+  f[2] = u.z;
+  f[3] = u.w;
+}
+
+template <typename T, int D, bool HALF, int PM, bool NORM>
+__global__ __launch_bounds__(kRopeThreads) void rope_bwd_kernel(
+    const T *__restrict__ q, int64_t qs, const T *__restrict__ k, int64_t ks, const float *dq_in,
+    const float *dk_in, const float *dv_in, float *dq, float *dk, float *dv,
+    const int32_t *__restrict__ tok_pos, const float *__restrict__ tcos,
+    const float *__restrict__ tsin, int64_t N, int H, int Hk, float eps) {
+  using RC = RopeChunk<float, D, HALF>;  // fp32 units of 4
+  constexpr int U = RC::U, NP = RC::NP, L = U / 2;
+  const int64_t gid = (int64_t)blockIdx.x * kRopeThreads + threadIdx.x;
+  const int64_t n = gid / L;
+  const int c = (int)(gid % L);
+  if (n >= N) return;  // whole token groups leave together
+  const int t = tok_pos[n];
+  float cs[2][NP], sn[2][NP];  // sin negated: the transpose rotates by -phi
+#pragma unroll
+  for (int par = 0; par < (PM ? 2 : 1); ++par) {
+    const int64_t pos = PM ? 2 * t + par : t;
+    const float *cr = tcos + pos * (D / 2), *sr = tsin + pos * (D / 2);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      cs[par][i] = cr[RC::col(c, i)];
+      sn[par][i] = -sr[RC::col(c, i)];
+    }
+  }
+  auto slot_head = [H](int hh) { return PM == 2 ? (hh & 1) * (H / 2) + hh / 2 : hh; };
+  auto rows = [&](const float *gin, float *gout, const T *x, int64_t xs, int nh) {
+    const uint4 *g4 = reinterpret_cast<const uint4 *>(gin + n * (int64_t)nh * D);
+    uint4 *o4 = reinterpret_cast<uint4 *>(gout + n * (int64_t)nh * D);
+    for (int hh = 0; hh < nh; ++hh) {
+      const int par = PM ? (hh & 1) : 0;
+      const int sb = slot_head(hh) * U;
+      uint4 r0, r1;
+      RC::rotate(g4[sb + c], g4[sb + c + U / 2], cs[par], sn[par], r0, r1);
+      if (NORM) {
+        float ga[4], gb[4], xa[4], xb[4];
+        unpack<float>(r0, ga);
+        unpack<float>(r1, gb);
+        const T *xr = x + n * xs + (int64_t)hh * D;
+        load4<T>(xr + 4 * c, xa);
+        load4<T>(xr + 4 * (c + U / 2), xb);
+        float ss = 0.0f, xg = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ss = fmaf(xa[i], xa[i], fmaf(xb[i], xb[i], ss));
+          xg = fmaf(xa[i], ga[i], fmaf(xb[i], gb[i], xg));
+        }
+        ss = lanes_sum<L>(ss);
+        xg = lanes_sum<L>(xg);
+        const float r = rsqrtf(ss * (1.0f / D) + eps);
+        const float cx = r * r * r * (1.0f / D) * xg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ga[i] = fmaf(r, ga[i], -cx * xa[i]);
+          gb[i] = fmaf(r, gb[i], -cx * xb[i]);
+        }
+        r0 = pack<float>(ga);
+        r1 = pack<float>(gb);
+      }
+      o4[hh * U + c] = r0;
+      o4[hh * U + c + U / 2] = r1;
+    }
+  };
+  rows(dq_in, dq, q, qs, H);
+  rows(dk_in, dk, k, ks, Hk);
+  if (dv) {
+    const uint4 *v4 = reinterpret_cast<const uint4 *>(dv_in + n * (int64_t)Hk * D);
+    uint4 *o4 = reinterpret_cast<uint4 *>(dv + n * (int64_t)Hk * D);
+    for (int hh = 0; hh < Hk; ++hh) {
+      const int sb = slot_head(hh) * U;
+      o4[hh * U + c] = v4[sb + c];
+      o4[hh * U + c + U / 2] = v4[sb + c + U / 2];
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_typed(const attn_plan *p, const void *q, int64_t qs, const void *k,
+                            int64_t ks, const float *dqi, const float *dki, const float *dvi,
+                            float *dq, float *dk, float *dv, hipStream_t stream) {
+  constexpr int L = D / 8;  // lanes per token
+  const int64_t N = p->p.N;
+  const dim3 grid((unsigned)((N * L + kRopeThreads - 1) / kRopeThreads));
+  const int32_t *pos = reinterpret_cast<const int32_t *>(p->ws + p->off_pos);
+  const float *tc = reinterpret_cast<const float *>(p->ws + p->off_cos);
+  const float *ts = reinterpret_cast<const float *>(p->ws + p->off_sin);
+  const T *Q = static_cast<const T *>(q);
+  const T *K = static_cast<const T *>(k);
+  const bool half = p->p.rope == ATTN_ROPE_HALF;
+  const int pm = p->p.paired;
+  const float eps = p->p.norm_eps;
+#define RB_LAUNCH(HF, PMV, NRM)                                                                 \
+  hipLaunchKernelGGL((rope_bwd_kernel<T, D, HF, PMV, NRM>), grid, dim3(kRopeThreads), 0, stream, \
+                     Q, qs, K, ks, dqi, dki, dvi, dq, dk, dv, pos, tc, ts, N, p->p.H, p->p.Hkv,  \
+                     eps)
+#define RB_PM(HF, NRM)                         \
+  do {                                         \
+    if (pm == 0) RB_LAUNCH(HF, 0, NRM);        \
+    else if (pm == 1) RB_LAUNCH(HF, 1, NRM);   \
+    else RB_LAUNCH(HF, 2, NRM);                \
+  } while (0)
+  if (p->p.qk_norm) {
+    if (half) RB_PM(true, true);
+    else RB_PM(false, true);
+  } else {
+    if (half) RB_PM(true, false);
+    else RB_PM(false, false);
+  }
+#undef RB_PM
+#undef RB_LAUNCH
+  return hipGetLastError();
+}
+
 }  // namespace
+
+attn_status launch_rope_bwd(const attn_plan *p, const void *q, int64_t qs, const void *k,
+                            int64_t ks, const float *dq_in, const float *dk_in,
+                            const float *dv_in, float *dq, float *dk, float *dv,
+                            hipStream_t stream) {
+  hipError_t e;
+  const bool bf = p->p.dtype == ATTN_BF16;
+  if (p->p.d == 64)
+    e = bf ? launch_bwd_typed<__bf16, 64>(p, q, qs, k, ks, dq_in, dk_in, dv_in, dq, dk, dv, stream)
+           : launch_bwd_typed<float, 64>(p, q, qs, k, ks, dq_in, dk_in, dv_in, dq, dk, dv, stream);
+  else
+    e = bf ? launch_bwd_typed<__bf16, 128>(p, q, qs, k, ks, dq_in, dk_in, dv_in, dq, dk, dv,
+                                           stream)
+           : launch_bwd_typed<float, 128>(p, q, qs, k, ks, dq_in, dk_in, dv_in, dq, dk, dv,
+                                          stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
 
 attn_status launch_rope(const attn_plan *p, const void *q, int64_t qs, const void *k, int64_t ks,
                         const void *v, int64_t vs, void *q_out, void *k_out, void *v_out,
