@@ -236,12 +236,19 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dkv_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * b + i;
-          float p = fast_exp2(fmaf(s[r], scale_log2, -lv[i]));
-          if (!full && (qr + i > qhi || qr + i < qlo)) p = 0.0f;
-          s[r] = p;
-          dp[r] = p * (dp[r] - dv4[i]);
+          s[r] = fast_exp2(fmaf(s[r], scale_log2, -lv[i]));
+          dp[r] -= dv4[i];
         }
       }
+      if (!full) {  // tiles on the diagonal, the window edge or the range end
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = 32 * rho + 8 * (r / 4) + 4 * h + (r % 4);
+          if (q > qhi || q < qlo) s[r] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] *= s[r];
       const bf16x8 pa[2] = {to_bf16x8(s, 0), to_bf16x8(s, 8)};
       const bf16x8 da[2] = {to_bf16x8(dp, 0), to_bf16x8(dp, 8)};
 #pragma unroll
@@ -370,12 +377,16 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dq_kernel(
         dp[beta] = mfma32x32x16(load_bf16x8(&cur.v[(32 * beta + l32) * RS + 16 * c + 8 * h]),
                                 gf[c], dp[beta]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(fmaf(s[beta][r], scale_log2, -lse2));
-        const int rel = 32 * beta + 8 * (r / 4) + (r % 4);
-        if (!full && (rel > khi || rel < klo)) p = 0.0f;
-        dp[beta][r] = p * (dp[beta][r] - dd);
+      for (int r = 0; r < 16; ++r) s[beta][r] = fast_exp2(fmaf(s[beta][r], scale_log2, -lse2));
+      if (!full) {  // tiles on the diagonal, the window edge or the range end
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rel = 32 * beta + 8 * (r / 4) + (r % 4);
+          if (rel > khi || rel < klo) s[beta][r] = 0.0f;
+        }
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[beta][r] = s[beta][r] * (dp[beta][r] - dd);
     }
 #pragma unroll
     for (int dl = 0; dl < D / 32; ++dl)
