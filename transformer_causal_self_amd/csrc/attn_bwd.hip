@@ -135,7 +135,7 @@ struct DkvBuf {
   __bf16 qt[D * TS];
   __bf16 gt[D * TS];
   float lse2[BQ];  // LSE * log2(e)
-  float dl[BQ];    // D
+  float dl[BQ];    // -D (the start value of the dP accumulator)
 };
 template <int D>
 struct DkvSmem {
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dkv_kernel(
     if (tid < 2 * BQ) {
       const int row = q0 + (tid % BQ);
       st_lse = row < it.k1 ? (tid < BQ ? LSE[(int64_t)it.head * Ns + row] * kLog2e
-                                       : delta[(int64_t)it.head * Ns + row])
+                                       : -delta[(int64_t)it.head * Ns + row])
                            : 0.0f;
     }
   };
@@ -218,27 +218,30 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dkv_kernel(
     const int qhi = min(it.k1 - 1, window > 0 ? kj + window - 1 : (1 << 30)) - qt0;
 #pragma unroll
     for (int rho = 0; rho < BQ / 32; ++rho) {
+      // rows of s: query 32*rho + 8b + 4h + i of the tile; column: key kj.
+      // dP starts from -D of its rows, so the MFMA leaves dP - D.
+      floatx16 s = {}, dp;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float4 d4 = *reinterpret_cast<const float4 *>(&cur.dl[32 * rho + 8 * b + 4 * h]);
+        dp[4 * b] = d4.x;
+        dp[4 * b + 1] = d4.y;
+        dp[4 * b + 2] = d4.z;
+        dp[4 * b + 3] = d4.w;
+      }
       // S first: its exponentials can start while dP is multiplied
-      floatx16 s = {}, dp = {};
 #pragma unroll
       for (int c = 0; c < D / 16; ++c)
         s = mfma32x32x16(load_bf16x8(&cur.q[(32 * rho + l32) * RS + 16 * c + 8 * h]), kf[c], s);
 #pragma unroll
       for (int c = 0; c < D / 16; ++c)
         dp = mfma32x32x16(load_bf16x8(&cur.g[(32 * rho + l32) * RS + 16 * c + 8 * h]), vf[c], dp);
-      // rows of s: query 32*rho + 8b + 4h + i of the tile; column: key kj
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int qr = 32 * rho + 8 * b + 4 * h;
-        const float4 l4 = *reinterpret_cast<const float4 *>(&cur.lse2[qr]);
-        const float4 d4 = *reinterpret_cast<const float4 *>(&cur.dl[qr]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float4 l4 = *reinterpret_cast<const float4 *>(&cur.lse2[32 * rho + 8 * b + 4 * h]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * b + i;
-          s[r] = fast_exp2(fmaf(s[r], scale_log2, -lv[i]));
-          dp[r] -= dv4[i];
-        }
+        for (int i = 0; i < 4; ++i) s[4 * b + i] = fast_exp2(fmaf(s[4 * b + i], scale_log2, -lv[i]));
       }
       if (!full) {  // tiles on the diagonal, the window edge or the range end
 #pragma unroll
@@ -335,7 +338,14 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dq_kernel(
     }
   }
   const float lse2 = qok ? LSE[(int64_t)it.head * Ns + qi] * kLog2e : 0.0f;
-  const float dd = qok ? delta[(int64_t)it.head * Ns + qi] : 0.0f;
+  // -D of this lane's query: the start value of every dP accumulator, so the
+  // MFMA leaves dP - D
+  floatx16 negd;
+  {
+    const float dd = qok ? delta[(int64_t)it.head * Ns + qi] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negd[r] = -dd;
+  }
   floatx16 dq[D / 32];
 #pragma unroll
   for (int dl = 0; dl < D / 32; ++dl) dq[dl] = floatx16{};
@@ -367,7 +377,8 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dq_kernel(
     floatx16 s[2], dp[2];
 #pragma unroll
     for (int beta = 0; beta < 2; ++beta) {
-      s[beta] = dp[beta] = floatx16{};
+      s[beta] = floatx16{};
+      dp[beta] = negd;
 #pragma unroll
       for (int c = 0; c < D / 16; ++c)
         s[beta] = mfma32x32x16(load_bf16x8(&cur.k[(32 * beta + l32) * RS + 16 * c + 8 * h]), qf[c],
@@ -386,7 +397,7 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dq_kernel(
         }
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dp[beta][r] = s[beta][r] * (dp[beta][r] - dd);
+      for (int r = 0; r < 16; ++r) dp[beta][r] *= s[beta][r];
     }
 #pragma unroll
     for (int dl = 0; dl < D / 32; ++dl)
