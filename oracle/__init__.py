@@ -231,3 +231,28 @@ def attn_bwd_gqa(q, k, v, dout, cu, causal=1, window=0, scale=0.0):
                             scale)
     G = H // Hkv
     return dq, dke.reshape(N, Hkv, G, d).sum(axis=2), dve.reshape(N, Hkv, G, d).sum(axis=2)
+
+
+# ------------------------------------------------------------------ fp8 in --
+# FP8 Q/K/V inputs ("Paired Head Attention", section 5 on the interplay with
+# other mechanisms: in FP8 training the paired layers take Q/K/V from a packed
+# FP8 projection).  The e4m3 format
+# (OCP FP8, "fn" variant): sign bit, 4 exponent bits with bias 7, 3 mantissa
+# bits; exponent field 0 gives subnormals m/8 * 2^-6; the code S.1111.111 is
+# NaN; there is no infinity.  Decoded values are multiplied by a per-tensor
+# scale.
+
+def fp8_e4m3_decode(codes):
+    """uint8 codes -> float64 values, from the format definition."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return sign * val
+
+
+def dequant_fp8(codes, scale):
+    """[N, H, d] uint8 e4m3 codes times the per-tensor scale (fp64)."""
+    return fp8_e4m3_decode(codes) * float(scale)
