@@ -1,7 +1,8 @@
 """Benchmark of the rotary causal self-attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--paired P]
-                    [--kv-heads G] [--qk-norm] [--rope-bwd] [--no-cpu-baseline]
+                    [--kv-heads G] [--qk-norm] [--rope-bwd] [--fp8-inputs]
+                    [--no-cpu-baseline]
 
 One step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: rope_qkv (Q, K rotated), attn_fwd (O, LSE) and, for
@@ -50,6 +51,9 @@ def parse():
                     help="RMS-normalise Q and K rows inside rope_qkv")
     ap.add_argument("--rope-bwd", action="store_true",
                     help="add rope_qkv_bwd (gradients back to the raw Q, K) to a backward step")
+    ap.add_argument("--fp8-inputs", action="store_true",
+                    help="Q, K, V arrive as e4m3 codes with per-tensor scales: the rotary "
+                         "step is rope_qkv_fp8 (dequantise, rotate, bf16 Q', K', V')")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -80,7 +84,7 @@ def stored_traffic(kernel, workload, digest):
     return r.get("bytes_per_launch")
 
 
-def cpu_baseline(w, inp, seconds, norm=False):
+def cpu_baseline(w, inp, seconds, norm=False, fp8=None):
     """fp64 oracle on a bounded random sample of the forward's query rows (plus
     its RoPE of every token), scaled to causal TFLOP/s."""
     import numpy as np
@@ -97,9 +101,13 @@ def cpu_baseline(w, inp, seconds, norm=False):
         return min(n, w.window) if w.window > 0 else n
 
     rng = np.random.default_rng(0)
-    q = inp["q"].double().numpy()
-    k = inp["k"].double().numpy()
-    v = inp["v"].double().numpy()
+    if fp8 is None:
+        q = inp["q"].double().numpy()
+        k = inp["k"].double().numpy()
+        v = inp["v"].double().numpy()
+    else:
+        q, k, v = (oracle.dequant_fp8(fp8[n].numpy(), s)
+                   for n, s in zip(("q", "k", "v"), fp8["scales"]))
 
     def rows_sample(nrows):
         return np.stack([rng.integers(0, Hs, nrows), rng.integers(0, Ns, nrows)], 1)
@@ -155,7 +163,10 @@ def main():
     if args.kv_heads is not None:
         import dataclasses
         w = dataclasses.replace(w, kv_heads=args.kv_heads)
-    copy_v = w.paired == 2      # V' must be written in the slot layout
+    if args.fp8_inputs and (w.dtype != wl.DTYPE_BF16 or args.rope_bwd):
+        sys.exit("--fp8-inputs needs a bf16 problem and no --rope-bwd")
+    # V' is written when it must be in the slot layout, or dequantised from FP8
+    copy_v = w.paired == 2 or args.fp8_inputs
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = wl.generate(w)
@@ -166,6 +177,9 @@ def main():
                                 num_kv_heads=w.kv_heads, qk_norm=int(args.qk_norm)).bind(dev)
     info = plan.info
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    fp8 = wl.fp8_tensors(w) if args.fp8_inputs else None
+    if fp8 is not None:
+        q8, k8, v8 = (fp8[n].to(dev) for n in ("q", "k", "v"))
     do = inp["do"].to(dev) if w.backward else None
     q2, k2 = torch.empty_like(q), torch.empty_like(k)
     v2 = torch.empty_like(v) if copy_v else v
@@ -173,7 +187,9 @@ def main():
     lse = torch.empty((info["attn_heads"], info["slots"]), dtype=torch.float32, device=dev)
     grads = None
     def rope():
-        if copy_v:
+        if fp8 is not None:
+            tca.rope_qkv_fp8(plan, q8, k8, v8, fp8["scales"], q_out=q2, k_out=k2, v_out=v2)
+        elif copy_v:
             tca.rope_qkv(plan, q, k, v, q_out=q2, k_out=k2, v_out=v2)
         else:
             tca.rope_qkv(plan, q, k, q_out=q2, k_out=k2)
@@ -238,9 +254,14 @@ def main():
     kern_ms = {n: sum(a.elapsed_time(b) for a, b in events[n]) / len(events[n]) for n in names}
     digest = kernel_sources_digest()
     wname = f"problem{w.num}" + ("" if args.paired is None else f"-paired{w.paired}") + (
-        "" if args.kv_heads is None else f"-kv{w.kv_heads}") + ("-qknorm" if args.qk_norm else "")
-    # rope_qkv algorithmic bytes: Q, K read and written (plus V when copied)
+        "" if args.kv_heads is None else f"-kv{w.kv_heads}") + (
+        "-qknorm" if args.qk_norm else "") + ("-fp8" if fp8 is not None else "")
+    # rope_qkv algorithmic bytes: Q, K read and written (plus V when copied);
+    # with FP8 inputs one byte read and two written per element of Q, K, V
+    kvh = w.kv_heads or w.heads
     rope_bytes = info["rope_bytes"] * (1.5 if copy_v else 1.0)
+    if fp8 is not None:
+        rope_bytes = 3.0 * w.n_tokens * w.head_dim * (w.heads + 2 * kvh)
     # rope_qkv_bwd: fp32 gradients of Q', K' read and of Q, K written, plus the
     # raw Q, K read again for the norm's gradient
     qk_elems = info["rope_bytes"] / 2 / (2 if w.dtype == wl.DTYPE_BF16 else 4)
@@ -279,12 +300,14 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == wl.DTYPE_BF16 else "fp32",
-        "data": "synthetic (seeded N(0,1) Q, K, V, dO; fixed sequence layout)",
+        "data": "synthetic (seeded N(0,1) Q, K, V, dO; fixed sequence layout"
+                + ("; Q, K, V quantised to e4m3 per tensor)" if fp8 is not None else ")"),
         "config": {"workload": w.name, "tokens": w.n_tokens, "heads": w.heads,
                    "head_dim": w.head_dim, "sequences": len(inp["cu"]) - 1,
                    "window": w.window, "paired": w.paired, "v_copied_by_rope": copy_v,
                    "kv_heads": w.kv_heads or w.heads,
                    "qk_norm": bool(args.qk_norm),
+                   "inputs": "fp8 e4m3 + per-tensor scales" if fp8 is not None else "bf16",
                    "rope": {1: "half-split", 2: "adjacent"}.get(w.rope, "none"),
                    "step": "+".join(names), "parallelism": "single GPU"},
         "roofline": roof,
@@ -297,7 +320,7 @@ def main():
         "kernel_sources": digest,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds, args.qk_norm)
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds, args.qk_norm, fp8)
     print(json.dumps(out), flush=True)
 
 

@@ -201,6 +201,29 @@ attn_status rope_qkv(const attn_plan *plan, const void *q, int64_t q_tok_stride,
                      void *k_out, void *v_out, void *stream);
 
 /*
+ * rope_qkv with FP8 inputs, for the FP8 packed-QKV training path ("Paired
+ * Head Attention" article, section 5, interplay with other mechanisms).  The
+ * pages do not fix the format or scaling; this entry reads them as e4m3 codes
+ * with one scale per tensor, dequantised in the rotary kernel so that no bf16
+ * copy of the projection output is written first.  q, k, v hold e4m3 codes (OCP
+ * FP8: sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities,
+ * S.1111.111 is NaN) as bytes [N, H, d] / [N, Hkv, d] rows at token strides
+ * q_tok_stride, k_tok_stride, v_tok_stride (in bytes = elements); element
+ * value = decoded code * scales[i] (scales: host array of 3 floats for q, k,
+ * v, read before the call returns).  The dequantised rows then go through
+ * exactly rope_qkv's steps (QK norm if set, rotation, adjacent permutation)
+ * and are stored as bf16 q_out, k_out [N, H, d] / [N, Hkv, d]; v_out (bf16
+ * [N, Hkv, d], required) is the dequantised V in slot order.
+ * bf16 plans only (ATTN_E_UNSUPPORTED otherwise).  Input pointers and strides
+ * must be multiples of 8 bytes, outputs 16-byte aligned (ATTN_E_ALIGN);
+ * outputs must not overlap the inputs; non-finite scales are ATTN_E_INVALID.
+ */
+attn_status rope_qkv_fp8(const attn_plan *plan, const void *q, int64_t q_tok_stride,
+                         const void *k, int64_t k_tok_stride, const void *v,
+                         int64_t v_tok_stride, const float *scales, void *q_out, void *k_out,
+                         void *v_out, void *stream);
+
+/*
  * Forward attention over the plan's sequences and mask (flash-style: the
  * N' x N' score matrix never reaches HBM; "Upgrading a textbook decoder",
  * section 4).  q, o: dense [N, H, d], k, v: dense [N, Hkv, d], in the plan's

@@ -86,6 +86,8 @@ def load_library():
     lib.attn_plan_work_items.argtypes = [vp, i32, ctypes.POINTER(i32), i64, ctypes.POINTER(i64)]
     lib.rope_qkv.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, vp, vp, vp]
     lib.rope_qkv_bwd.argtypes = [vp, vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp]
+    lib.rope_qkv_fp8.argtypes = [vp, vp, i64, vp, i64, vp, i64, ctypes.POINTER(ctypes.c_float),
+                                 vp, vp, vp, vp]
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.attn_status_str.argtypes = [ctypes.c_int]
@@ -93,7 +95,7 @@ def load_library():
     lib.attn_plan_destroy.argtypes = [vp]
     lib.attn_plan_destroy.restype = None
     for f in ("attn_plan_create", "attn_plan_bind", "attn_plan_stats", "attn_plan_work_items",
-              "rope_qkv", "rope_qkv_bwd", "attn_fwd", "attn_bwd"):
+              "rope_qkv", "rope_qkv_bwd", "rope_qkv_fp8", "attn_fwd", "attn_bwd"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -228,6 +230,31 @@ def rope_qkv(plan: Plan, q, k, v=None, q_out=None, k_out=None, v_out=None):
         v.data_ptr() if v_out is not None else None, vs, q_out.data_ptr(), k_out.data_ptr(),
         v_out.data_ptr() if v_out is not None else None, _stream(q.device)))
     return (q_out, k_out) if v_out is None else (q_out, k_out, v_out)
+
+
+def rope_qkv_fp8(plan: Plan, q, k, v, scales, q_out=None, k_out=None, v_out=None):
+    """rope_qkv on FP8 e4m3 inputs (uint8 codes or torch.float8_e4m3fn, [N, H, d] /
+    [N, Hkv, d] rows) with per-tensor scales (q, k, v).  Returns bf16 (q', k', v')."""
+    p = plan.problem
+    H, Hkv, d = p["num_heads"], p["num_kv_heads"], p["head_dim"]
+    codes = []
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        if x.dtype == torch.float8_e4m3fn:
+            x = x.view(torch.uint8)
+        _need(plan, x, name, torch.uint8, dense=False)
+        codes.append(x)
+    q, k, v = codes
+    qs, ks, vs = _token_stride(q, H, d), _token_stride(k, Hkv, d), _token_stride(v, Hkv, d)
+    mk = lambda t, heads: torch.empty((q.shape[0], heads, d), dtype=torch.bfloat16,
+                                      device=q.device) if t is None else t
+    q_out, k_out, v_out = mk(q_out, H), mk(k_out, Hkv), mk(v_out, Hkv)
+    for name, x, kv in (("q_out", q_out, False), ("k_out", k_out, True), ("v_out", v_out, True)):
+        _need(plan, x, name, kv=kv)
+    sc = (ctypes.c_float * 3)(*[float(x) for x in scales])
+    _check("rope_qkv_fp8", load_library().rope_qkv_fp8(
+        plan.handle, q.data_ptr(), qs, k.data_ptr(), ks, v.data_ptr(), vs, sc,
+        q_out.data_ptr(), k_out.data_ptr(), v_out.data_ptr(), _stream(q.device)))
+    return q_out, k_out, v_out
 
 
 def rope_qkv_bwd(plan: Plan, d_q, d_k, q=None, k=None, d_v=None, dq_out=None, dk_out=None,

@@ -12,6 +12,10 @@ attn_status launch_rope(const attn_plan *p, const void *q, int64_t qs, const voi
                         const void *v, int64_t vs, void *q_out, void *k_out, void *v_out,
                         hipStream_t stream);
 
+attn_status launch_rope_fp8(const attn_plan *p, const void *q, int64_t qs, const void *k,
+                            int64_t ks, const void *v, int64_t vs, const float *scales,
+                            void *q_out, void *k_out, void *v_out, hipStream_t stream);
+
 attn_status launch_rope_bwd(const attn_plan *p, const void *q, int64_t qs, const void *k,
                             int64_t ks, const float *dq_in, const float *dk_in, const float *dv_in,
                             float *dq, float *dk, float *dv, hipStream_t stream);

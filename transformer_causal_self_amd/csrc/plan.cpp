@@ -385,6 +385,30 @@ attn_status rope_qkv(const attn_plan *p, const void *q, int64_t qs, const void *
                            static_cast<hipStream_t>(stream));
 }
 
+attn_status rope_qkv_fp8(const attn_plan *p, const void *q, int64_t qs, const void *k,
+                         int64_t ks, const void *v, int64_t vs, const float *scales, void *q_out,
+                         void *k_out, void *v_out, void *stream) {
+  if (!p) return ATTN_E_INVALID;
+  if (p->p.rope == ATTN_ROPE_NONE) return ATTN_E_INVALID;
+  if (p->p.dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
+  if (!p->ws) return ATTN_E_WORKSPACE;
+  if (!scales) return ATTN_E_INVALID;
+  for (int i = 0; i < 3; ++i)
+    if (!std::isfinite(scales[i])) return ATTN_E_INVALID;
+  if (p->p.N == 0) return ATTN_OK;
+  const int64_t row = (int64_t)p->p.H * p->p.d;
+  const int64_t kv_row = (int64_t)p->p.Hkv * p->p.d;
+  if (!q || !k || !v || !q_out || !k_out || !v_out) return ATTN_E_INVALID;
+  if (qs < row || ks < kv_row || vs < kv_row) return ATTN_E_INVALID;
+  // one load covers 8 codes
+  const auto a8 = [](const void *x) { return (reinterpret_cast<uintptr_t>(x) & 7) == 0; };
+  if (qs % 8 || ks % 8 || vs % 8 || !a8(q) || !a8(k) || !a8(v)) return ATTN_E_ALIGN;
+  if (!aligned16(q_out) || !aligned16(k_out) || !aligned16(v_out)) return ATTN_E_ALIGN;
+  if (q_out == q || k_out == k || v_out == v) return ATTN_E_INVALID;
+  return attn::launch_rope_fp8(p, q, qs, k, ks, v, vs, scales, q_out, k_out, v_out,
+                               static_cast<hipStream_t>(stream));
+}
+
 attn_status rope_qkv_bwd(const attn_plan *p, const void *q, int64_t qs, const void *k,
                          int64_t ks, const float *d_q, const float *d_k, const float *d_v,
                          float *dq_out, float *dk_out, float *dv_out, void *stream) {

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
     const float *__restrict__ tcos, const float *__restrict__ tsin, int64_t N, int H, int Hk,
     float eps) {
   using RC = RopeChunk<T, D, HALF>;
-  constexpr int V = RC::V, U = RC::U, NP = RC::NP;
+  constexpr int U = RC::U, NP = RC::NP;
   const int64_t gid = (int64_t)blockIdx.x * kRopeThreads + threadIdx.x;
   const int64_t n = gid / (U / 2);
   const int c = (int)(gid % (U / 2));
@@ -315,6 +315,126 @@ hipError_t launch_typed(const attn_plan *p, const void *q, int64_t qs, const voi
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ fp8 in --
+// FP8 (e4m3, OCP) inputs with per-tensor scales, bf16 outputs: the same lane
+// split as the bf16 kernel (lane = token x units c, c + U/2 of 8 outputs),
+// each unit read as 8 one-byte codes, decoded by v_cvt_pk_f32_fp8 and scaled
+// before the norm and the rotation.  V is decoded and copied (its slot order
+// under the adjacent pairing).
+__device__ __forceinline__ void unpack_fp8(const uint2 &u, float scale, float *f) {
+  const uint32_t w[2] = {u.x, u.y};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);  // bytes 0, 1
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);   // bytes 2, 3
+    f[4 * i] = lo[0] * scale;
+    f[4 * i + 1] = lo[1] * scale;
+    f[4 * i + 2] = hi[0] * scale;
+    f[4 * i + 3] = hi[1] * scale;
+  }
+}
+
+template <int D, bool HALF, int PM, bool NORM>
+__global__ __launch_bounds__(kRopeThreads) void rope_fp8_kernel(
+    const uint8_t *__restrict__ q, int64_t qs, const uint8_t *__restrict__ k, int64_t ks,
+    const uint8_t *__restrict__ v, int64_t vs, __bf16 *__restrict__ qo, __bf16 *__restrict__ ko,
+    __bf16 *__restrict__ vo, const int32_t *__restrict__ tok_pos, const float *__restrict__ tcos,
+    const float *__restrict__ tsin, int64_t N, int H, int Hk, float eps, float q_scale,
+    float k_scale, float v_scale) {
+  using RC = RopeChunk<__bf16, D, HALF>;
+  constexpr int U = RC::U, NP = RC::NP;  // units of 8 elements
+  const int64_t gid = (int64_t)blockIdx.x * kRopeThreads + threadIdx.x;
+  const int64_t n = gid / (U / 2);
+  const int c = (int)(gid % (U / 2));
+  if (n >= N) return;  // whole token groups leave together
+  const int t = tok_pos[n];
+  float cs[2][NP], sn[2][NP];
+#pragma unroll
+  for (int par = 0; par < (PM ? 2 : 1); ++par) {
+    const int64_t pos = PM ? 2 * t + par : t;
+    const float *cr = tcos + pos * (D / 2), *sr = tsin + pos * (D / 2);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      cs[par][i] = cr[RC::col(c, i)];
+      sn[par][i] = sr[RC::col(c, i)];
+    }
+  }
+  auto out_head = [H](int hh) { return PM == 2 ? (hh & 1) * (H / 2) + hh / 2 : hh; };
+  auto rows = [&](const uint8_t *src, int64_t ss, float scale, __bf16 *dst, int nh) {
+    const uint2 *s8 = reinterpret_cast<const uint2 *>(src + n * ss);  // 8 codes per unit
+    uint4 *d4 = reinterpret_cast<uint4 *>(dst + n * (int64_t)nh * D);
+    for (int hh = 0; hh < nh; ++hh) {
+      const int par = PM ? (hh & 1) : 0;
+      float a[8], b[8];
+      unpack_fp8(s8[hh * U + c], scale, a);
+      unpack_fp8(s8[hh * U + c + U / 2], scale, b);
+      float r = 1.0f;
+      if (NORM) {
+        float ss2 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss2 = fmaf(a[i], a[i], fmaf(b[i], b[i], ss2));
+        r = rsqrtf(lanes_sum<U / 2>(ss2) * (1.0f / D) + eps);
+      }
+      uint4 r0, r1;
+      RC::rotate_vals(a, b, cs[par], sn[par], r, r0, r1);
+      const int ob = out_head(hh) * U;
+      d4[ob + c] = r0;
+      d4[ob + c + U / 2] = r1;
+    }
+  };
+  rows(q, qs, q_scale, qo, H);
+  rows(k, ks, k_scale, ko, Hk);
+  const uint2 *v8 = reinterpret_cast<const uint2 *>(v + n * vs);
+  uint4 *v4 = reinterpret_cast<uint4 *>(vo + n * (int64_t)Hk * D);
+  for (int hh = 0; hh < Hk; ++hh) {
+    float a[8], b[8];
+    unpack_fp8(v8[hh * U + c], v_scale, a);
+    unpack_fp8(v8[hh * U + c + U / 2], v_scale, b);
+    const int ob = out_head(hh) * U;
+    v4[ob + c] = pack<__bf16>(a);
+    v4[ob + c + U / 2] = pack<__bf16>(b);
+  }
+}
+
+template <int D>
+hipError_t launch_fp8_typed(const attn_plan *p, const void *q, int64_t qs, const void *k,
+                            int64_t ks, const void *v, int64_t vs, const float *scales, void *qo,
+                            void *ko, void *vo, hipStream_t stream) {
+  constexpr int C = D / 16;  // lanes per token
+  const int64_t N = p->p.N;
+  const dim3 grid((unsigned)((N * C + kRopeThreads - 1) / kRopeThreads));
+  const int32_t *pos = reinterpret_cast<const int32_t *>(p->ws + p->off_pos);
+  const float *tc = reinterpret_cast<const float *>(p->ws + p->off_cos);
+  const float *ts = reinterpret_cast<const float *>(p->ws + p->off_sin);
+  const uint8_t *Q = static_cast<const uint8_t *>(q), *K = static_cast<const uint8_t *>(k);
+  const uint8_t *Vv = static_cast<const uint8_t *>(v);
+  __bf16 *QO = static_cast<__bf16 *>(qo), *KO = static_cast<__bf16 *>(ko);
+  __bf16 *VO = static_cast<__bf16 *>(vo);
+  const bool half = p->p.rope == ATTN_ROPE_HALF;
+  const int pm = p->p.paired;
+  const float eps = p->p.norm_eps;
+#define F8_LAUNCH(HF, PMV, NRM)                                                                 \
+  hipLaunchKernelGGL((rope_fp8_kernel<D, HF, PMV, NRM>), grid, dim3(kRopeThreads), 0, stream, Q, \
+                     qs, K, ks, Vv, vs, QO, KO, VO, pos, tc, ts, N, p->p.H, p->p.Hkv, eps,       \
+                     scales[0], scales[1], scales[2])
+#define F8_PM(HF, NRM)                         \
+  do {                                         \
+    if (pm == 0) F8_LAUNCH(HF, 0, NRM);        \
+    else if (pm == 1) F8_LAUNCH(HF, 1, NRM);   \
+    else F8_LAUNCH(HF, 2, NRM);                \
+  } while (0)
+  if (p->p.qk_norm) {
+    if (half) F8_PM(true, true);
+    else F8_PM(false, true);
+  } else {
+    if (half) F8_PM(true, false);
+    else F8_PM(false, false);
+  }
+#undef F8_PM
+#undef F8_LAUNCH
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- backward --
 // Backward of rope_qkv for one token per group of D/8 lanes: the incoming
 // gradient rows (fp32, read from the slot layout) are rotated by -phi, the
@@ -454,6 +574,16 @@ hipError_t launch_bwd_typed(const attn_plan *p, const void *q, int64_t qs, const
 }
 
 }  // namespace
+
+attn_status launch_rope_fp8(const attn_plan *p, const void *q, int64_t qs, const void *k,
+                            int64_t ks, const void *v, int64_t vs, const float *scales,
+                            void *q_out, void *k_out, void *v_out, hipStream_t stream) {
+  const hipError_t e =
+      p->p.d == 64
+          ? launch_fp8_typed<64>(p, q, qs, k, ks, v, vs, scales, q_out, k_out, v_out, stream)
+          : launch_fp8_typed<128>(p, q, qs, k, ks, v, vs, scales, q_out, k_out, v_out, stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
 
 attn_status launch_rope_bwd(const attn_plan *p, const void *q, int64_t qs, const void *k,
                             int64_t ks, const float *dq_in, const float *dk_in,

@@ -12,6 +12,10 @@ Recipe (stated once, used everywhere):
   * tensors: ``torch.Generator().manual_seed(seed)``; ``randn`` in float32 of
     shape [N, H, d], drawn in the order Q, K, V, dO; cast to bfloat16 with
     round-to-nearest-even when the problem is bf16.
+  * FP8 inputs (``fp8_tensors``): the same float32 draws for Q, K, V, each
+    tensor divided by its scale amax / 448 (float32) and cast to
+    ``torch.float8_e4m3fn`` (the codes and the scales are the inputs; the
+    cast only draws them).
   * seed: the problem number 1..5 unless a test picks another.
 """
 from dataclasses import dataclass, replace
@@ -108,5 +112,24 @@ def tensors(w: Workload, seed: Optional[int] = None, with_grad: Optional[bool] =
 def generate(w: Workload, seed: Optional[int] = None, with_grad: Optional[bool] = None):
     """All inputs of one problem: dict with cu (numpy int32) and the tensors."""
     out = tensors(w, seed, with_grad)
+    out["cu"] = cu_seqlens(w, seed)
+    return out
+
+
+def fp8_tensors(w: Workload, seed: Optional[int] = None):
+    """Q, K, V as e4m3 codes (uint8 CPU tensors, shapes as in ``tensors``) and their
+    per-tensor float32 scales (q, k, v)."""
+    seed = w.num if seed is None else seed
+    g = torch.Generator().manual_seed(seed)
+    shape = (w.n_tokens, w.heads, w.head_dim)
+    kv_shape = (w.n_tokens, w.kv_heads or w.heads, w.head_dim)
+    out, scales = {}, []
+    for n in ("q", "k", "v"):
+        x = torch.randn(kv_shape if n in ("k", "v") else shape, generator=g, dtype=torch.float32)
+        amax = float(x.abs().max()) if x.numel() else 1.0
+        sc = float(np.float32(max(amax, 1e-30) / 448.0))
+        out[n] = (x / sc).to(torch.float8_e4m3fn).view(torch.uint8)
+        scales.append(sc)
+    out["scales"] = tuple(scales)
     out["cu"] = cu_seqlens(w, seed)
     return out
