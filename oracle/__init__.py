@@ -36,8 +36,8 @@ def _load():
                                     _I64, ctypes.POINTER(ctypes.c_int)]
     lib.oracle_rope.argtypes = [_D, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _I32, ctypes.c_int,
                                 ctypes.c_int, ctypes.c_double, ctypes.c_int, _D]
-    common = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, _I32, ctypes.c_int, ctypes.c_int,
-              ctypes.c_int, ctypes.c_int, ctypes.c_double]
+    common = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _I32, ctypes.c_int,
+              ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double]
     lib.oracle_attn_fwd.argtypes = [_D, _D, _D] + common + [_D, _D]
     lib.oracle_attn_fwd_rows.argtypes = [_D, _D, _D] + common + [ctypes.c_int64, _I64, _D, _D]
     lib.oracle_attn_bwd.argtypes = [_D, _D, _D, _D] + common + [_D, _D, _D]
@@ -137,56 +137,73 @@ def _heads(H, N, paired):
     return (H // 2, 2 * N) if paired else (H, N)
 
 
+def _vdim(q, k, v):
+    N, H, d = q.shape
+    if k.shape != q.shape or v.ndim != 3 or v.shape[:2] != (N, H):
+        raise ValueError("q, k must be [N, H, d] and v [N, H, dv]")
+    return v.shape[2]
+
+
 def attn_fwd(q, k, v, cu, paired=0, causal=1, window=0, scale=0.0):
-    """O [N, H, d] and LSE [H', N'] of softmax(scale q k^T + mask) v."""
+    """O [N, H, dv] and LSE [H', N'] of softmax(scale q k^T + mask) v (q, k: [N, H, d])."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     cu = np.ascontiguousarray(cu, dtype=np.int32)
     N, H, d = q.shape
+    dv = _vdim(q, k, v)
     Hs, Ns = _heads(H, N, paired)
-    o = np.empty_like(q)
+    o = np.empty((N, H, dv), dtype=np.float64)
     lse = np.empty((Hs, Ns), dtype=np.float64)
-    _check(_load().oracle_attn_fwd(_p(q), _p(k), _p(v), N, H, d, _p(cu, _I32), len(cu) - 1, paired,
-                                   causal, window, scale, _p(o), _p(lse)), "oracle_attn_fwd")
+    _check(_load().oracle_attn_fwd(_p(q), _p(k), _p(v), N, H, d, dv, _p(cu, _I32), len(cu) - 1,
+                                   paired, causal, window, scale, _p(o), _p(lse)),
+           "oracle_attn_fwd")
     return o, lse
 
 
 def attn_fwd_rows(q, k, v, cu, rows, paired=0, causal=1, window=0, scale=0.0):
-    """Forward at selected (attention head, slot) rows: O rows [R, d], LSE [R]."""
+    """Forward at selected (attention head, slot) rows: O rows [R, dv], LSE [R]."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     cu = np.ascontiguousarray(cu, dtype=np.int32)
     rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 2)
     N, H, d = q.shape
-    o = np.empty((len(rows), d), dtype=np.float64)
+    dv = _vdim(q, k, v)
+    o = np.empty((len(rows), dv), dtype=np.float64)
     lse = np.empty(len(rows), dtype=np.float64)
-    _check(_load().oracle_attn_fwd_rows(_p(q), _p(k), _p(v), N, H, d, _p(cu, _I32), len(cu) - 1,
-                                        paired, causal, window, scale, len(rows), _p(rows, _I64),
-                                        _p(o), _p(lse)), "oracle_attn_fwd_rows")
+    _check(_load().oracle_attn_fwd_rows(_p(q), _p(k), _p(v), N, H, d, dv, _p(cu, _I32),
+                                        len(cu) - 1, paired, causal, window, scale, len(rows),
+                                        _p(rows, _I64), _p(o), _p(lse)), "oracle_attn_fwd_rows")
     return o, lse
 
 
 def attn_bwd(q, k, v, dout, cu, paired=0, causal=1, window=0, scale=0.0):
-    """dQ, dK, dV [N, H, d] of L = sum(O * dout)."""
+    """dQ, dK [N, H, d] and dV [N, H, dv] of L = sum(O * dout)."""
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     cu = np.ascontiguousarray(cu, dtype=np.int32)
     N, H, d = q.shape
-    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
-    _check(_load().oracle_attn_bwd(_p(q), _p(k), _p(v), _p(dout), N, H, d, _p(cu, _I32),
+    w = _vdim(q, k, v)
+    if dout.shape != v.shape:
+        raise ValueError("dout must be shaped like v")
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(v)
+    _check(_load().oracle_attn_bwd(_p(q), _p(k), _p(v), _p(dout), N, H, d, w, _p(cu, _I32),
                                    len(cu) - 1, paired, causal, window, scale, _p(dq), _p(dk),
                                    _p(dv)), "oracle_attn_bwd")
     return dq, dk, dv
 
 
 def attn_bwd_sampled(q, k, v, dout, cu, q_rows, k_cols, paired=0, causal=1, window=0, scale=0.0):
-    """dQ at (head, slot) rows [R, d]; dK, dV at (head, slot) key columns [C, d]."""
+    """dQ at (head, slot) rows [R, d]; dK [C, d], dV [C, dv] at (head, slot) key columns."""
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     cu = np.ascontiguousarray(cu, dtype=np.int32)
     q_rows = np.ascontiguousarray(q_rows, dtype=np.int64).reshape(-1, 2)
     k_cols = np.ascontiguousarray(k_cols, dtype=np.int64).reshape(-1, 2)
     N, H, d = q.shape
+    w = _vdim(q, k, v)
+    if dout.shape != v.shape:
+        raise ValueError("dout must be shaped like v")
     dq = np.empty((len(q_rows), d), dtype=np.float64)
     dk = np.empty((len(k_cols), d), dtype=np.float64)
-    dv = np.empty((len(k_cols), d), dtype=np.float64)
-    _check(_load().oracle_attn_bwd_sampled(_p(q), _p(k), _p(v), _p(dout), N, H, d, _p(cu, _I32),
+    dv = np.empty((len(k_cols), w), dtype=np.float64)
+    _check(_load().oracle_attn_bwd_sampled(_p(q), _p(k), _p(v), _p(dout), N, H, d, w,
+                                           _p(cu, _I32),
                                            len(cu) - 1, paired, causal, window, scale,
                                            len(q_rows), _p(q_rows, _I64), _p(dq), len(k_cols),
                                            _p(k_cols, _I64), _p(dk), _p(dv)),
@@ -227,10 +244,11 @@ def attn_bwd_gqa(q, k, v, dout, cu, causal=1, window=0, scale=0.0):
     """dQ [N, H, d]; dK, dV [N, Hkv, d] (each K/V head gathers its group's gradients)."""
     H = np.shape(q)[1]
     N, Hkv, d = np.shape(k)
+    dv = np.shape(v)[2]
     dq, dke, dve = attn_bwd(q, expand_kv(k, H), expand_kv(v, H), dout, cu, 0, causal, window,
                             scale)
     G = H // Hkv
-    return dq, dke.reshape(N, Hkv, G, d).sum(axis=2), dve.reshape(N, Hkv, G, d).sum(axis=2)
+    return dq, dke.reshape(N, Hkv, G, d).sum(axis=2), dve.reshape(N, Hkv, G, dv).sum(axis=2)
 
 
 # ------------------------------------------------------------------ fp8 in --

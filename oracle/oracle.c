@@ -38,7 +38,13 @@
  *    the norm itself: "Upgrading a textbook decoder", section 1 "RMSNorm",
  *    x / sqrt(mean(x^2) + eps) with eps = 1e-6.
  *
- * Conventions: tensors are row-major [N, H, d] (token, head, feature).
+ *  - Separate value width: "Paired Head Attention" article, section "Source 1:
+ *    model configuration" (each attention module takes its own qk_dim and
+ *    v_dim): q, k carry d features and v, dO, O, dV carry dv; the scores use
+ *    q . k over d, the output sums P v over dv.
+ *
+ * Conventions: tensors are row-major [N, H, d] (token, head, feature); v and
+ * the tensors shaped like it are [N, H, dv].
  * paired = 0: slot = token, attention head = h.
  * paired = 1: slot = 2 t + h / (H/2), attention head = h mod (H/2)
  *             (the article's code: view of [T, H, d] as [2T, H/2, d]).
@@ -232,12 +238,13 @@ int oracle_rms_norm_bwd(const double *x, const double *dy, int64_t rows, int d, 
 
 typedef struct {
   int64_t N, Ns;     /* tokens, slots */
-  int H, Hs, d;      /* heads given, attention heads, head dim */
+  int H, Hs, d, dv;  /* heads given, attention heads, q/k head dim, v head dim */
   int paired, causal, window;
   double scale;
   int S;
   int64_t *cus;      /* slot boundaries, S + 1 entries */
-  double *q, *k, *v, *g; /* gathered [Hs][Ns][d]; g = dO (may be NULL) */
+  double *q, *k;     /* gathered [Hs][Ns][d] */
+  double *v, *g;     /* gathered [Hs][Ns][dv]; g = dO (may be NULL) */
 } problem;
 
 static void problem_free(problem *p) {
@@ -248,41 +255,43 @@ static void problem_free(problem *p) {
   free(p->g);
 }
 
-/* Gather a logical [N, H, d] tensor into [Hs][Ns][d] slot order. */
-static void gather(const double *src, const problem *p, double *dst) {
+/* Gather a logical [N, H, w] tensor into [Hs][Ns][w] slot order. */
+static void gather(const double *src, const problem *p, int w, double *dst) {
 #pragma omp parallel for schedule(static)
   for (int64_t n = 0; n < p->N; ++n)
     for (int h = 0; h < p->H; ++h) {
       int64_t s;
       int j;
       oracle_slot_map(n, h, p->H, p->paired, &s, &j);
-      memcpy(dst + ((int64_t)j * p->Ns + s) * p->d, src + (n * p->H + h) * (int64_t)p->d,
-             sizeof(double) * (size_t)p->d);
+      memcpy(dst + ((int64_t)j * p->Ns + s) * w, src + (n * p->H + h) * (int64_t)w,
+             sizeof(double) * (size_t)w);
     }
 }
 
-/* Scatter [Hs][Ns][d] slot order back to a logical [N, H, d] tensor. */
-static void scatter(const double *src, const problem *p, double *dst) {
+/* Scatter [Hs][Ns][w] slot order back to a logical [N, H, w] tensor. */
+static void scatter(const double *src, const problem *p, int w, double *dst) {
 #pragma omp parallel for schedule(static)
   for (int64_t n = 0; n < p->N; ++n)
     for (int h = 0; h < p->H; ++h) {
       int64_t s;
       int j;
       oracle_slot_map(n, h, p->H, p->paired, &s, &j);
-      memcpy(dst + (n * p->H + h) * (int64_t)p->d, src + ((int64_t)j * p->Ns + s) * p->d,
-             sizeof(double) * (size_t)p->d);
+      memcpy(dst + (n * p->H + h) * (int64_t)w, src + ((int64_t)j * p->Ns + s) * w,
+             sizeof(double) * (size_t)w);
     }
 }
 
 static int problem_init(problem *p, const double *q, const double *k, const double *v,
-                        const double *dout, int64_t N, int H, int d, const int32_t *cu, int S,
-                        int paired, int causal, int window, double scale) {
+                        const double *dout, int64_t N, int H, int d, int dv, const int32_t *cu,
+                        int S, int paired, int causal, int window, double scale) {
   memset(p, 0, sizeof(*p));
-  if (!q || !k || !v || !check_shape(N, H, d, paired) || !check_cu(cu, S, N)) return OR_EINVAL;
+  if (!q || !k || !v || !check_shape(N, H, d, paired) || dv < 1 || !check_cu(cu, S, N))
+    return OR_EINVAL;
   if (window > 0 && !causal) return OR_EINVAL;
   p->N = N;
   p->H = H;
   p->d = d;
+  p->dv = dv;
   p->paired = paired;
   p->Hs = paired ? H / 2 : H;
   p->Ns = paired ? 2 * N : N;
@@ -291,20 +300,21 @@ static int problem_init(problem *p, const double *q, const double *k, const doub
   p->scale = (scale == 0.0) ? 1.0 / sqrt((double)d) : scale;
   p->S = S;
   const size_t elems = (size_t)p->Ns * (size_t)p->Hs * (size_t)d;
+  const size_t velems = (size_t)p->Ns * (size_t)p->Hs * (size_t)dv;
   p->cus = (int64_t *)malloc(sizeof(int64_t) * (size_t)(S + 1));
   p->q = (double *)malloc(sizeof(double) * (elems ? elems : 1));
   p->k = (double *)malloc(sizeof(double) * (elems ? elems : 1));
-  p->v = (double *)malloc(sizeof(double) * (elems ? elems : 1));
-  if (dout) p->g = (double *)malloc(sizeof(double) * (elems ? elems : 1));
+  p->v = (double *)malloc(sizeof(double) * (velems ? velems : 1));
+  if (dout) p->g = (double *)malloc(sizeof(double) * (velems ? velems : 1));
   if (!p->cus || !p->q || !p->k || !p->v || (dout && !p->g)) {
     problem_free(p);
     return OR_ENOMEM;
   }
   for (int i = 0; i <= S; ++i) p->cus[i] = (int64_t)cu[i] * (paired ? 2 : 1);
-  gather(q, p, p->q);
-  gather(k, p, p->k);
-  gather(v, p, p->v);
-  if (dout) gather(dout, p, p->g);
+  gather(q, p, d, p->q);
+  gather(k, p, d, p->k);
+  gather(v, p, dv, p->v);
+  if (dout) gather(dout, p, dv, p->g);
   return OR_OK;
 }
 
@@ -369,38 +379,38 @@ static int64_t max_doc_len(const problem *p) {
   return mx;
 }
 
-/* Forward of one row: o (d values) and lse. */
+/* Forward of one row: o (dv values) and lse. */
 static void fwd_row(const problem *p, int j, int64_t i, double *z, double *o, double *lse) {
-  const int d = p->d;
+  const int dv = p->dv;
   const int doc = doc_of(p, i);
   const int64_t b = p->cus[doc], e = p->cus[doc + 1];
   double m, l;
   score_row(p, j, i, z, &m, &l);
-  for (int c = 0; c < d; ++c) o[c] = 0.0;
+  for (int c = 0; c < dv; ++c) o[c] = 0.0;
   for (int64_t jj = b; jj < e; ++jj) {
     if (z[jj - b] == -INFINITY) continue;
     const double pij = exp(z[jj - b] - m) / l;
-    const double *vj = p->v + ((int64_t)j * p->Ns + jj) * d;
-    for (int c = 0; c < d; ++c) o[c] += pij * vj[c];
+    const double *vj = p->v + ((int64_t)j * p->Ns + jj) * dv;
+    for (int c = 0; c < dv; ++c) o[c] += pij * vj[c];
   }
   *lse = m + log(l);
 }
 
 /*
- * Full forward.  q, k, v, o: [N, H, d] (q and k already rotated); lse: [H', N'].
- * scale == 0 selects 1 / sqrt(d).
+ * Full forward.  q, k: [N, H, d] (already rotated); v, o: [N, H, dv]; lse:
+ * [H', N'].  scale == 0 selects 1 / sqrt(d).
  */
 int oracle_attn_fwd(const double *q, const double *k, const double *v, int64_t N, int H, int d,
-                    const int32_t *cu, int S, int paired, int causal, int window, double scale,
-                    double *o, double *lse) {
+                    int dv, const int32_t *cu, int S, int paired, int causal, int window,
+                    double scale, double *o, double *lse) {
   problem p;
-  int rc = problem_init(&p, q, k, v, NULL, N, H, d, cu, S, paired, causal, window, scale);
+  int rc = problem_init(&p, q, k, v, NULL, N, H, d, dv, cu, S, paired, causal, window, scale);
   if (rc) return rc;
   if (!o || !lse) {
     problem_free(&p);
     return OR_EINVAL;
   }
-  const size_t elems = (size_t)p.Ns * (size_t)p.Hs * (size_t)d;
+  const size_t elems = (size_t)p.Ns * (size_t)p.Hs * (size_t)dv;
   double *os = (double *)malloc(sizeof(double) * (elems ? elems : 1));
   if (!os) {
     problem_free(&p);
@@ -418,10 +428,10 @@ int oracle_attn_fwd(const double *q, const double *k, const double *v, int64_t N
 #pragma omp for schedule(dynamic, 16) collapse(2)
     for (int j = 0; j < p.Hs; ++j)
       for (int64_t i = 0; i < p.Ns; ++i)
-        if (z) fwd_row(&p, j, i, z, os + ((int64_t)j * p.Ns + i) * d, lse + (int64_t)j * p.Ns + i);
+        if (z) fwd_row(&p, j, i, z, os + ((int64_t)j * p.Ns + i) * dv, lse + (int64_t)j * p.Ns + i);
     free(z);
   }
-  if (!fail) scatter(os, &p, o);
+  if (!fail) scatter(os, &p, dv, o);
   free(os);
   problem_free(&p);
   return fail ? OR_ENOMEM : OR_OK;
@@ -429,14 +439,14 @@ int oracle_attn_fwd(const double *q, const double *k, const double *v, int64_t N
 
 /*
  * Forward of selected rows only.  rows holds nrows pairs (attention head j,
- * slot i).  o_rows: [nrows, d]; lse_rows: [nrows].
+ * slot i).  o_rows: [nrows, dv]; lse_rows: [nrows].
  */
 int oracle_attn_fwd_rows(const double *q, const double *k, const double *v, int64_t N, int H,
-                         int d, const int32_t *cu, int S, int paired, int causal, int window,
-                         double scale, int64_t nrows, const int64_t *rows, double *o_rows,
-                         double *lse_rows) {
+                         int d, int dv, const int32_t *cu, int S, int paired, int causal,
+                         int window, double scale, int64_t nrows, const int64_t *rows,
+                         double *o_rows, double *lse_rows) {
   problem p;
-  int rc = problem_init(&p, q, k, v, NULL, N, H, d, cu, S, paired, causal, window, scale);
+  int rc = problem_init(&p, q, k, v, NULL, N, H, d, dv, cu, S, paired, causal, window, scale);
   if (rc) return rc;
   for (int64_t r = 0; r < nrows; ++r)
     if (rows[2 * r] < 0 || rows[2 * r] >= p.Hs || rows[2 * r + 1] < 0 || rows[2 * r + 1] >= p.Ns) {
@@ -454,7 +464,7 @@ int oracle_attn_fwd_rows(const double *q, const double *k, const double *v, int6
     }
 #pragma omp for schedule(dynamic, 1)
     for (int64_t r = 0; r < nrows; ++r)
-      if (z) fwd_row(&p, (int)rows[2 * r], rows[2 * r + 1], z, o_rows + r * d, lse_rows + r);
+      if (z) fwd_row(&p, (int)rows[2 * r], rows[2 * r + 1], z, o_rows + r * dv, lse_rows + r);
     free(z);
   }
   problem_free(&p);
@@ -470,33 +480,33 @@ int oracle_attn_fwd_rows(const double *q, const double *k, const double *v, int6
  */
 static void stats_row(const problem *p, int j, int64_t i, double *z, double *m, double *l,
                       double *D) {
-  const int d = p->d;
+  const int dv = p->dv;
   const int doc = doc_of(p, i);
   const int64_t b = p->cus[doc], e = p->cus[doc + 1];
   score_row(p, j, i, z, m, l);
-  const double *gi = p->g + ((int64_t)j * p->Ns + i) * d;
+  const double *gi = p->g + ((int64_t)j * p->Ns + i) * dv;
   double acc = 0.0;
   for (int64_t jj = b; jj < e; ++jj) {
     if (z[jj - b] == -INFINITY) continue;
     const double pij = exp(z[jj - b] - *m) / *l;
-    acc += pij * dot(gi, p->v + ((int64_t)j * p->Ns + jj) * d, d);
+    acc += pij * dot(gi, p->v + ((int64_t)j * p->Ns + jj) * dv, dv);
   }
   *D = acc; /* dO_i . O_i = sum_jj P_ij (dO_i . v_jj) */
 }
 
 /* dQ_i = scale * sum_jj P_ij (dO_i . v_jj - D_i) k_jj. */
 static void dq_row(const problem *p, int j, int64_t i, double *z, double *dq) {
-  const int d = p->d;
+  const int d = p->d, dv = p->dv;
   const int doc = doc_of(p, i);
   const int64_t b = p->cus[doc], e = p->cus[doc + 1];
   double m, l, D;
   stats_row(p, j, i, z, &m, &l, &D);
-  const double *gi = p->g + ((int64_t)j * p->Ns + i) * d;
+  const double *gi = p->g + ((int64_t)j * p->Ns + i) * dv;
   for (int c = 0; c < d; ++c) dq[c] = 0.0;
   for (int64_t jj = b; jj < e; ++jj) {
     if (z[jj - b] == -INFINITY) continue;
     const double pij = exp(z[jj - b] - m) / l;
-    const double dp = dot(gi, p->v + ((int64_t)j * p->Ns + jj) * d, d);
+    const double dp = dot(gi, p->v + ((int64_t)j * p->Ns + jj) * dv, dv);
     const double ds = pij * (dp - D);
     const double *kj = p->k + ((int64_t)j * p->Ns + jj) * d;
     for (int c = 0; c < d; ++c) dq[c] += p->scale * ds * kj[c];
@@ -510,23 +520,22 @@ static void dq_row(const problem *p, int j, int64_t i, double *z, double *dq) {
  */
 static void dkv_col(const problem *p, int j, int64_t jj, const double *m, const double *l,
                     const double *D, double *dk, double *dv) {
-  const int d = p->d;
+  const int d = p->d, w = p->dv;
   const int doc = doc_of(p, jj);
   const int64_t b = p->cus[doc], e = p->cus[doc + 1];
   const double *kj = p->k + ((int64_t)j * p->Ns + jj) * d;
-  const double *vj = p->v + ((int64_t)j * p->Ns + jj) * d;
-  for (int c = 0; c < d; ++c) dk[c] = dv[c] = 0.0;
+  const double *vj = p->v + ((int64_t)j * p->Ns + jj) * w;
+  for (int c = 0; c < d; ++c) dk[c] = 0.0;
+  for (int c = 0; c < w; ++c) dv[c] = 0.0;
   for (int64_t i = b; i < e; ++i) {
     if (!visible(p, i, jj, b, e)) continue;
     const double *qi = p->q + ((int64_t)j * p->Ns + i) * d;
-    const double *gi = p->g + ((int64_t)j * p->Ns + i) * d;
+    const double *gi = p->g + ((int64_t)j * p->Ns + i) * w;
     const double zz = p->scale * dot(qi, kj, d);
     const double pij = exp(zz - m[i]) / l[i];
-    const double ds = pij * (dot(gi, vj, d) - D[i]);
-    for (int c = 0; c < d; ++c) {
-      dv[c] += pij * gi[c];
-      dk[c] += p->scale * ds * qi[c];
-    }
+    const double ds = pij * (dot(gi, vj, w) - D[i]);
+    for (int c = 0; c < w; ++c) dv[c] += pij * gi[c];
+    for (int c = 0; c < d; ++c) dk[c] += p->scale * ds * qi[c];
   }
 }
 
@@ -553,24 +562,25 @@ static int all_stats(const problem *p, double *m, double *l, double *D, const un
 }
 
 /*
- * Full backward.  Inputs q, k, v, dout: [N, H, d] (q, k rotated).  Outputs
- * dq, dk, dv: [N, H, d], gradients of sum(O * dout) with respect to q, k, v.
+ * Full backward.  Inputs q, k: [N, H, d] (rotated), v, dout: [N, H, dvd].
+ * Outputs dq, dk: [N, H, d], dv: [N, H, dvd], gradients of sum(O * dout) with
+ * respect to q, k, v.
  */
 int oracle_attn_bwd(const double *q, const double *k, const double *v, const double *dout,
-                    int64_t N, int H, int d, const int32_t *cu, int S, int paired, int causal,
-                    int window, double scale, double *dq, double *dk, double *dv) {
+                    int64_t N, int H, int d, int dvd, const int32_t *cu, int S, int paired,
+                    int causal, int window, double scale, double *dq, double *dk, double *dv) {
   if (!dout || !dq || !dk || !dv) return OR_EINVAL;
   problem p;
-  int rc = problem_init(&p, q, k, v, dout, N, H, d, cu, S, paired, causal, window, scale);
+  int rc = problem_init(&p, q, k, v, dout, N, H, d, dvd, cu, S, paired, causal, window, scale);
   if (rc) return rc;
   const size_t rowsn = (size_t)p.Hs * (size_t)p.Ns;
-  const size_t elems = rowsn * (size_t)d;
+  const size_t elems = rowsn * (size_t)d, velems = rowsn * (size_t)dvd;
   double *m = (double *)malloc(sizeof(double) * (rowsn ? rowsn : 1));
   double *l = (double *)malloc(sizeof(double) * (rowsn ? rowsn : 1));
   double *D = (double *)malloc(sizeof(double) * (rowsn ? rowsn : 1));
   double *dqs = (double *)malloc(sizeof(double) * (elems ? elems : 1));
   double *dks = (double *)malloc(sizeof(double) * (elems ? elems : 1));
-  double *dvs = (double *)malloc(sizeof(double) * (elems ? elems : 1));
+  double *dvs = (double *)malloc(sizeof(double) * (velems ? velems : 1));
   int fail = !m || !l || !D || !dqs || !dks || !dvs;
   if (!fail) fail = all_stats(&p, m, l, D, NULL);
   if (!fail) {
@@ -593,13 +603,13 @@ int oracle_attn_bwd(const double *q, const double *k, const double *v, const dou
       for (int64_t jj = 0; jj < p.Ns; ++jj) {
         const int64_t base = (int64_t)j * p.Ns;
         dkv_col(&p, j, jj, m + base, l + base, D + base, dks + (base + jj) * d,
-                dvs + (base + jj) * d);
+                dvs + (base + jj) * dvd);
       }
   }
   if (!fail) {
-    scatter(dqs, &p, dq);
-    scatter(dks, &p, dk);
-    scatter(dvs, &p, dv);
+    scatter(dqs, &p, d, dq);
+    scatter(dks, &p, d, dk);
+    scatter(dvs, &p, dvd, dv);
   }
   free(m);
   free(l);
@@ -613,17 +623,19 @@ int oracle_attn_bwd(const double *q, const double *k, const double *v, const dou
 
 /*
  * Backward at selected points.  q_rows: nq pairs (head j, slot i) -> dq_rows
- * [nq, d]; k_cols: nk pairs (head j, slot jj) -> dk_cols, dv_cols [nk, d].
- * Row statistics are computed only for rows that see a requested key.
+ * [nq, d]; k_cols: nk pairs (head j, slot jj) -> dk_cols [nk, d], dv_cols
+ * [nk, dv].  Row statistics are computed only for rows that see a requested
+ * key.
  */
 int oracle_attn_bwd_sampled(const double *q, const double *k, const double *v,
-                            const double *dout, int64_t N, int H, int d, const int32_t *cu,
-                            int S, int paired, int causal, int window, double scale, int64_t nq,
-                            const int64_t *q_rows, double *dq_rows, int64_t nk,
-                            const int64_t *k_cols, double *dk_cols, double *dv_cols) {
+                            const double *dout, int64_t N, int H, int d, int dv,
+                            const int32_t *cu, int S, int paired, int causal, int window,
+                            double scale, int64_t nq, const int64_t *q_rows, double *dq_rows,
+                            int64_t nk, const int64_t *k_cols, double *dk_cols,
+                            double *dv_cols) {
   if (!dout) return OR_EINVAL;
   problem p;
-  int rc = problem_init(&p, q, k, v, dout, N, H, d, cu, S, paired, causal, window, scale);
+  int rc = problem_init(&p, q, k, v, dout, N, H, d, dv, cu, S, paired, causal, window, scale);
   if (rc) return rc;
   for (int64_t r = 0; r < nq; ++r)
     if (q_rows[2 * r] < 0 || q_rows[2 * r] >= p.Hs || q_rows[2 * r + 1] < 0 ||
@@ -674,7 +686,7 @@ int oracle_attn_bwd_sampled(const double *q, const double *k, const double *v,
         const int j = (int)k_cols[2 * r];
         const int64_t base = (int64_t)j * p.Ns;
         dkv_col(&p, j, k_cols[2 * r + 1], m + base, l + base, D + base, dk_cols + r * d,
-                dv_cols + r * d);
+                dv_cols + r * dv);
       }
     }
     free(need);

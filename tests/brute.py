@@ -59,14 +59,14 @@ def dense_mask(cu, mult, causal, window):
 
 
 def attention(q, k, v, cu, paired=0, causal=1, window=0, scale=0.0):
-    """Dense fp64 forward: O [N, H, d], LSE [H', N'], and P per attention head."""
+    """Dense fp64 forward: O [N, H, dv], LSE [H', N'], and P per attention head."""
     N, H, d = q.shape
     s = scale if scale else 1.0 / np.sqrt(d)
     qs, origin = interleave(q, H, paired)
     ks, _ = interleave(k, H, paired)
     vs, _ = interleave(v, H, paired)
     mask = dense_mask(list(cu), 2 if paired else 1, causal, window)
-    o = np.zeros_like(q, dtype=np.float64)
+    o = np.zeros((N, H, v.shape[2]), dtype=np.float64)
     lses, probs = [], []
     for j in range(len(qs)):
         z = s * (qs[j] @ ks[j].T)
