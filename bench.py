@@ -1,7 +1,7 @@
 """Benchmark of the rotary causal self-attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--paired P]
-                    [--kv-heads G] [--qk-norm] [--rope-bwd] [--fp8-inputs]
+                    [--kv-heads G] [--v-dim DV] [--qk-norm] [--rope-bwd] [--fp8-inputs]
                     [--no-cpu-baseline]
 
 One step is one pass of the whole hot path over one batch of synthetic input
@@ -47,6 +47,8 @@ def parse():
                          "where rope_qkv also copies V in the slot layout)")
     ap.add_argument("--kv-heads", type=int, default=None,
                     help="grouped-query attention: number of K/V heads (divides the heads)")
+    ap.add_argument("--v-dim", type=int, default=None,
+                    help="width of V, O and dO rows (64 or 128) when it differs from head_dim")
     ap.add_argument("--qk-norm", action="store_true",
                     help="RMS-normalise Q and K rows inside rope_qkv")
     ap.add_argument("--rope-bwd", action="store_true",
@@ -138,7 +140,8 @@ def cpu_baseline(w, inp, seconds, norm=False, fp8=None):
     kr = oracle.qk_prep(k, cu, w.rope, w.rope_base, w.paired, norm)
     fwd_rows(qr, kr, rows)
     dt = time.perf_counter() - t0
-    flops = sum(4.0 * w.head_dim * visible(int(s)) for s in rows[:, 1])
+    flops = sum(2.0 * (w.head_dim + (w.v_dim or w.head_dim)) * visible(int(s))
+                for s in rows[:, 1])
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"{n} random (head, query) rows of this workload's forward (causal FLOPs "
@@ -163,6 +166,9 @@ def main():
     if args.kv_heads is not None:
         import dataclasses
         w = dataclasses.replace(w, kv_heads=args.kv_heads)
+    if args.v_dim is not None:
+        import dataclasses
+        w = dataclasses.replace(w, v_dim=args.v_dim)
     if args.fp8_inputs and (w.dtype != wl.DTYPE_BF16 or args.rope_bwd):
         sys.exit("--fp8-inputs needs a bf16 problem and no --rope-bwd")
     # V' is written when it must be in the slot layout, or dequantised from FP8
@@ -174,7 +180,8 @@ def main():
                                 "fp32" if w.dtype == wl.DTYPE_FP32 else "bf16", inp["cu"],
                                 causal=w.causal, window=w.window, softmax_scale=w.scale,
                                 rope=w.rope, rope_base=w.rope_base, paired=w.paired,
-                                num_kv_heads=w.kv_heads, qk_norm=int(args.qk_norm)).bind(dev)
+                                num_kv_heads=w.kv_heads, qk_norm=int(args.qk_norm),
+                                v_head_dim=w.v_dim).bind(dev)
     info = plan.info
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
     fp8 = wl.fp8_tensors(w) if args.fp8_inputs else None
@@ -183,7 +190,7 @@ def main():
     do = inp["do"].to(dev) if w.backward else None
     q2, k2 = torch.empty_like(q), torch.empty_like(k)
     v2 = torch.empty_like(v) if copy_v else v
-    o = torch.empty_like(q)
+    o = torch.empty((q.shape[0], q.shape[1], v.shape[2]), dtype=q.dtype, device=dev)
     lse = torch.empty((info["attn_heads"], info["slots"]), dtype=torch.float32, device=dev)
     grads = None
     def rope():
@@ -255,13 +262,16 @@ def main():
     digest = kernel_sources_digest()
     wname = f"problem{w.num}" + ("" if args.paired is None else f"-paired{w.paired}") + (
         "" if args.kv_heads is None else f"-kv{w.kv_heads}") + (
+        "" if args.v_dim is None else f"-dv{w.v_dim}") + (
         "-qknorm" if args.qk_norm else "") + ("-fp8" if fp8 is not None else "")
     # rope_qkv algorithmic bytes: Q, K read and written (plus V when copied);
     # with FP8 inputs one byte read and two written per element of Q, K, V
     kvh = w.kv_heads or w.heads
-    rope_bytes = info["rope_bytes"] * (1.5 if copy_v else 1.0)
+    dv = w.v_dim or w.head_dim
+    es = 2 if w.dtype == wl.DTYPE_BF16 else 4
+    rope_bytes = info["rope_bytes"] + (2.0 * w.n_tokens * kvh * dv * es if copy_v else 0.0)
     if fp8 is not None:
-        rope_bytes = 3.0 * w.n_tokens * w.head_dim * (w.heads + 2 * kvh)
+        rope_bytes = 3.0 * w.n_tokens * ((w.heads + kvh) * w.head_dim + kvh * dv)
     # rope_qkv_bwd: fp32 gradients of Q', K' read and of Q, K written, plus the
     # raw Q, K read again for the norm's gradient
     qk_elems = info["rope_bytes"] / 2 / (2 if w.dtype == wl.DTYPE_BF16 else 4)
@@ -305,7 +315,7 @@ def main():
         "config": {"workload": w.name, "tokens": w.n_tokens, "heads": w.heads,
                    "head_dim": w.head_dim, "sequences": len(inp["cu"]) - 1,
                    "window": w.window, "paired": w.paired, "v_copied_by_rope": copy_v,
-                   "kv_heads": w.kv_heads or w.heads,
+                   "kv_heads": w.kv_heads or w.heads, "v_dim": dv,
                    "qk_norm": bool(args.qk_norm),
                    "inputs": "fp8 e4m3 + per-tensor scales" if fp8 is not None else "bf16",
                    "rope": {1: "half-split", 2: "adjacent"}.get(w.rope, "none"),

@@ -43,6 +43,11 @@
  *                      ...: head h at position (h mod 2) * H/2 + h / 2 of the
  *                      token's H*d row.
  *   K, V (grouped)     [N, Hkv, d] when num_kv_heads = Hkv < H (unpaired only).
+ *   V, O, dO, dV       rows of dv = v_head_dim elements instead of d when the
+ *                      problem sets a separate value width ("Paired Head
+ *                      Attention" article, section "Source 1: model
+ *                      configuration": each attention module has its own
+ *                      qk_dim and v_dim); Q, K, dQ, dK keep d.
  *   LSE                float [H', N'] (attention head, slot); natural log.
  *   dQ, dK, dV         float [N, H, d] (same slot view as Q when paired);
  *                      dK, dV are [N, Hkv, d] when grouped.
@@ -109,13 +114,17 @@ typedef struct {
                                 K head row over d, x / sqrt(mean(x^2) + eps), in
                                 fp32 and without a gain */
   float norm_eps;            /* eps of that norm; 0 selects 1e-6 */
+  int32_t v_head_dim;        /* dv, the width of V, O, dO and dV rows: 0 selects
+                                head_dim; else 64 or 128, and a value other than
+                                head_dim needs ATTN_BF16 (q, k keep head_dim) */
 } attn_problem;
 
 /* Counts for throughput and roofline reporting (exact, from the plan). */
 typedef struct {
   int64_t visible_pairs;     /* (query slot, key slot) pairs inside the mask, all heads */
-  double fwd_flops;          /* 4 * d * visible_pairs (QK^T and PV) */
-  double bwd_flops;          /* 2.5 * fwd_flops (five products) */
+  double fwd_flops;          /* 2 (d + dv) visible_pairs (QK^T and PV) */
+  double bwd_flops;          /* 2 (3 d + 2 dv) visible_pairs (five products: S, dP,
+                                dV, dQ, dK); 2.5 fwd_flops when dv = d */
   double rope_bytes;         /* read Q, K and write Q', K' once */
   double fwd_bytes;          /* read Q, K, V and write O, LSE once */
   double bwd_bytes;          /* read Q, K, V, O, dO, LSE and write dQ, dK, dV once */
@@ -125,6 +134,7 @@ typedef struct {
   int32_t attn_heads;        /* H' */
   int32_t max_positions;     /* rows of the rotary table */
   int32_t kv_heads;          /* K/V heads: Hkv, or H' when not grouped */
+  int32_t v_head_dim;        /* dv */
 } attn_plan_info;
 
 /*
@@ -133,8 +143,9 @@ typedef struct {
  * cos/sin table rounded to fp32, and the tile work lists (fully masked causal
  * and window tiles are never listed; longest items first).  Host only: makes
  * no HIP call.  On success *out owns a plan to free with attn_plan_destroy.
- * Errors: ATTN_E_INVALID (bad field), ATTN_E_UNSUPPORTED (head_dim not 64 or
- * 128), ATTN_E_NOMEM.
+ * Errors: ATTN_E_INVALID (bad field), ATTN_E_UNSUPPORTED (head_dim or
+ * v_head_dim not 64 or 128; v_head_dim != head_dim with fp32; grouped K/V
+ * heads with pairing), ATTN_E_NOMEM.
  */
 attn_status attn_plan_create(const attn_problem *problem, attn_plan **out);
 
@@ -183,9 +194,9 @@ attn_status attn_plan_work_items(const attn_plan *plan, int32_t which, int32_t *
  * QKV).  q_out, k_out: dense [N, H, d] and [N, Hkv, d]; q_out == q (in place)
  * is allowed when q_tok_stride == H*d, same for k.  Written dense, the outputs
  * already are the paired interleaved layout.
- * v / v_out: when v_out is not NULL, V ([N, Hkv, d], token stride
- * v_tok_stride) is copied dense into v_out in the same pass; when v_out is
- * NULL, v is ignored.
+ * v / v_out: when v_out is not NULL, V ([N, Hkv, dv], token stride
+ * v_tok_stride >= Hkv*dv) is copied dense into v_out in the same pass; when
+ * v_out is NULL, v is ignored.
  * ATTN_PAIRED_ADJACENT: the outputs are written in that layout's head order
  * (see Layouts), so v_out is required (V' feeds attn_fwd) and neither output
  * may alias its input (ATTN_E_INVALID otherwise).
@@ -207,13 +218,14 @@ attn_status rope_qkv(const attn_plan *plan, const void *q, int64_t q_tok_stride,
  * with one scale per tensor, dequantised in the rotary kernel so that no bf16
  * copy of the projection output is written first.  q, k, v hold e4m3 codes (OCP
  * FP8: sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities,
- * S.1111.111 is NaN) as bytes [N, H, d] / [N, Hkv, d] rows at token strides
- * q_tok_stride, k_tok_stride, v_tok_stride (in bytes = elements); element
+ * S.1111.111 is NaN) as bytes [N, H, d] / [N, Hkv, d] / [N, Hkv, dv] rows at
+ * token strides q_tok_stride, k_tok_stride, v_tok_stride (in bytes =
+ * elements); element
  * value = decoded code * scales[i] (scales: host array of 3 floats for q, k,
  * v, read before the call returns).  The dequantised rows then go through
  * exactly rope_qkv's steps (QK norm if set, rotation, adjacent permutation)
  * and are stored as bf16 q_out, k_out [N, H, d] / [N, Hkv, d]; v_out (bf16
- * [N, Hkv, d], required) is the dequantised V in slot order.
+ * [N, Hkv, dv], required) is the dequantised V in slot order.
  * bf16 plans only (ATTN_E_UNSUPPORTED otherwise).  Input pointers and strides
  * must be multiples of 8 bytes, outputs 16-byte aligned (ATTN_E_ALIGN);
  * outputs must not overlap the inputs; non-finite scales are ATTN_E_INVALID.
@@ -226,8 +238,9 @@ attn_status rope_qkv_fp8(const attn_plan *plan, const void *q, int64_t q_tok_str
 /*
  * Forward attention over the plan's sequences and mask (flash-style: the
  * N' x N' score matrix never reaches HBM; "Upgrading a textbook decoder",
- * section 4).  q, o: dense [N, H, d], k, v: dense [N, Hkv, d], in the plan's
- * dtype (q, k already rotated); lse: float [H', N'].  Every slot of o and lse
+ * section 4).  q: dense [N, H, d], k: [N, Hkv, d], v: [N, Hkv, dv], o:
+ * [N, H, dv], in the plan's dtype (q, k already rotated); lse: float
+ * [H', N'].  Every slot of o and lse
  * is written.
  */
 attn_status attn_fwd(const attn_plan *plan, const void *q, const void *k, const void *v, void *o,
@@ -238,13 +251,13 @@ attn_status attn_fwd(const attn_plan *plan, const void *q, const void *k, const 
  * values), recomputing P = exp(s q k^T - LSE):
  *     D_i = dO_i . O_i,  dS = P o (dO V^T - D),
  *     dV = P^T dO,  dQ = s dS K,  dK = s dS^T Q.
- * q, o, d_o: dense [N, H, d], k, v: dense [N, Hkv, d], in the plan's dtype;
- * lse: float [H', N'] as written by attn_fwd; dq: float [N, H, d], dk, dv:
- * float [N, Hkv, d], fully overwritten.  With grouped K/V heads, dK and dV of
- * a K/V head sum the contributions of every query head of its group (float
- * atomic adds, so their rounding order may differ between runs; without
- * grouping every output element is written once and results are
- * bit-reproducible).
+ * q: dense [N, H, d], k: [N, Hkv, d], v: [N, Hkv, dv], o, d_o: [N, H, dv], in
+ * the plan's dtype; lse: float [H', N'] as written by attn_fwd; dq: float
+ * [N, H, d], dk: float [N, Hkv, d], dv: float [N, Hkv, dv], fully overwritten.
+ * With grouped K/V heads, dK and dV of a K/V head sum the contributions of
+ * every query head of its group (float atomic adds, so their rounding order
+ * may differ between runs; without grouping every output element is written
+ * once and results are bit-reproducible).
  * bf16 only (ATTN_E_UNSUPPORTED for fp32).  Uses the workspace's scratch
  * area, so two attn_bwd calls sharing one workspace must not overlap.
  */
@@ -263,7 +276,8 @@ attn_status attn_bwd(const attn_plan *plan, const void *q, const void *k, const 
  * rope_qkv; ignored and may be NULL without qk_norm).
  * d_q: float [N', H', d] slot layout (= [N, H, d] memory), d_k: likewise with
  * Hkv heads; dq_out, dk_out: float [N, H, d] / [N, Hkv, d] in head order.
- * d_v / dv_out (optional, both or neither): dV copied from the slot layout
+ * d_v / dv_out (optional, both or neither; float [N, Hkv, dv]): dV copied
+ * from the slot layout
  * into head order (V is not rotated; this only matters for the adjacent
  * pairing, whose slot layout permutes heads).
  * Outputs may alias d_q / d_k / d_v except with ATTN_PAIRED_ADJACENT

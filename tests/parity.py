@@ -35,7 +35,7 @@ def make_plan(w, cu, device="cuda"):
                                 "fp32" if w.dtype == wl.DTYPE_FP32 else "bf16", cu,
                                 causal=w.causal, window=w.window, softmax_scale=w.scale,
                                 rope=w.rope, rope_base=w.rope_base, paired=w.paired,
-                                num_kv_heads=w.kv_heads).bind(device)
+                                num_kv_heads=w.kv_heads, v_head_dim=w.v_dim).bind(device)
 
 
 def f64(t):

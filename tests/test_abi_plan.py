@@ -71,11 +71,30 @@ def plan(**kw):
     (dict(qk_norm=1, norm_eps=-1e-6), -1),
     (dict(head_dim=32), -2),                           # valid, not covered by the kernels
     (dict(head_dim=96), -2),
+    (dict(v_head_dim=-64), -1),
+    (dict(v_head_dim=63), -1),
+    (dict(v_head_dim=96), -2),                         # value width not covered
+    (dict(v_head_dim=128, dtype="fp32"), -2),          # separate value width: bf16 only
 ])
 def test_plan_rejects(kw, status):
     with pytest.raises(tca.AttnError) as e:
         plan(**kw)
     assert e.value.status == status
+
+
+@pytest.mark.parametrize("d,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_value_width_counts(d, dv):
+    p = plan(num_tokens=100, cu_seqlens=[0, 40, 100], head_dim=d, v_head_dim=dv)
+    pairs = p.info["visible_pairs"]
+    assert pairs == 2 * (40 * 41 // 2 + 60 * 61 // 2)
+    assert p.info["v_head_dim"] == dv
+    assert p.info["fwd_flops"] == 2 * (d + dv) * pairs
+    assert p.info["bwd_flops"] == 2 * (3 * d + 2 * dv) * pairs
+    # Q, K read and written by the rotary pass; V is not part of it
+    assert p.info["rope_bytes"] == 2 * 2 * (100 * 2 * d) * 2
+    # forward: Q, K, V read, O written (bf16), LSE written (fp32)
+    assert p.info["fwd_bytes"] == 2 * 100 * 2 * (2 * d + 2 * dv) + 4 * 100 * 2
+    assert plan(v_head_dim=0).info["v_head_dim"] == 64
 
 
 def test_empty_problem_is_valid():

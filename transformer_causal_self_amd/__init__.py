@@ -49,7 +49,7 @@ class _Problem(ctypes.Structure):
                 ("softmax_scale", ctypes.c_float), ("rope", ctypes.c_int32),
                 ("rope_base", ctypes.c_double), ("paired", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("qk_norm", ctypes.c_int32),
-                ("norm_eps", ctypes.c_float)]
+                ("norm_eps", ctypes.c_float), ("v_head_dim", ctypes.c_int32)]
 
 
 class _Info(ctypes.Structure):
@@ -58,7 +58,8 @@ class _Info(ctypes.Structure):
                 ("fwd_bytes", ctypes.c_double), ("bwd_bytes", ctypes.c_double),
                 ("fwd_items", ctypes.c_int64), ("bwd_items", ctypes.c_int64),
                 ("slots", ctypes.c_int64), ("attn_heads", ctypes.c_int32),
-                ("max_positions", ctypes.c_int32), ("kv_heads", ctypes.c_int32)]
+                ("max_positions", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("v_head_dim", ctypes.c_int32)]
 
 
 _lib = None
@@ -169,7 +170,8 @@ class Plan:
 def attn_plan_create(num_tokens: int, num_heads: int, head_dim: int, dtype, cu_seqlens,
                      causal: int = 1, window: int = 0, softmax_scale: float = 0.0, rope="half",
                      rope_base: float = 10000.0, paired: int = 0,
-                     num_kv_heads: int = 0, qk_norm: int = 0, norm_eps: float = 0.0) -> Plan:
+                     num_kv_heads: int = 0, qk_norm: int = 0, norm_eps: float = 0.0,
+                     v_head_dim: int = 0) -> Plan:
     if isinstance(dtype, str):
         dtype = {"bf16": ATTN_BF16, "fp32": ATTN_FP32}[dtype]
     elif isinstance(dtype, torch.dtype):
@@ -179,14 +181,15 @@ def attn_plan_create(num_tokens: int, num_heads: int, head_dim: int, dtype, cu_s
                   cu_seqlens=cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                   num_seqs=len(cu) - 1, causal=causal, window=window,
                   softmax_scale=softmax_scale, rope=ROPE.get(rope, rope), rope_base=rope_base,
-                  paired=paired, num_kv_heads=num_kv_heads, qk_norm=qk_norm, norm_eps=norm_eps)
+                  paired=paired, num_kv_heads=num_kv_heads, qk_norm=qk_norm, norm_eps=norm_eps,
+                  v_head_dim=v_head_dim)
     h = ctypes.c_void_p()
     _check("attn_plan_create", load_library().attn_plan_create(ctypes.byref(pr), ctypes.byref(h)))
     problem = dict(num_tokens=num_tokens, num_heads=num_heads, head_dim=head_dim, dtype=dtype,
                    cu_seqlens=cu.copy(), causal=causal, window=window,
                    softmax_scale=softmax_scale, rope=ROPE.get(rope, rope), rope_base=rope_base,
                    paired=paired, num_kv_heads=num_kv_heads or num_heads, qk_norm=qk_norm,
-                   norm_eps=norm_eps)
+                   norm_eps=norm_eps, v_head_dim=v_head_dim or head_dim)
     return Plan(h.value, problem)
 
 
@@ -197,18 +200,20 @@ def _token_stride(x: torch.Tensor, H: int, d: int) -> int:
     return x.stride(0)
 
 
-def _need(plan: Plan, x: torch.Tensor, name: str, dtype=None, dense=True, kv=False):
+def _need(plan: Plan, x: torch.Tensor, name: str, dtype=None, dense=True, kv=False, vd=False):
+    """Check device, dtype and (dense) shape [N, H or Hkv (kv), d or dv (vd)]."""
     p = plan.problem
     heads = p["num_kv_heads"] if kv else p["num_heads"]
+    width = p["v_head_dim"] if vd else p["head_dim"]
     if plan.workspace is None:
         raise AttnError(name, -4)
     if not x.is_cuda or x.device != plan.workspace.device:
         raise ValueError(f"{name} must be on {plan.workspace.device}")
     if x.dtype != (dtype or plan.dtype):
         raise ValueError(f"{name} must be {dtype or plan.dtype}, got {x.dtype}")
-    if dense and (tuple(x.shape) != (p["num_tokens"], heads, p["head_dim"])
-                  or not x.is_contiguous()):
-        raise ValueError(f"{name} must be contiguous [N, {'Hkv' if kv else 'H'}, d]")
+    if dense and (tuple(x.shape) != (p["num_tokens"], heads, width) or not x.is_contiguous()):
+        raise ValueError(f"{name} must be contiguous [N, {'Hkv' if kv else 'H'}, "
+                         f"{'dv' if vd else 'd'}]")
 
 
 def rope_qkv(plan: Plan, q, k, v=None, q_out=None, k_out=None, v_out=None):
@@ -218,13 +223,14 @@ def rope_qkv(plan: Plan, q, k, v=None, q_out=None, k_out=None, v_out=None):
     for name, x in (("q", q), ("k", k)) + ((("v", v),) if v_out is not None else ()):
         _need(plan, x, name, dense=False)
     qs, ks = _token_stride(q, H, d), _token_stride(k, Hkv, d)
-    vs = _token_stride(v, Hkv, d) if v_out is not None else 0
+    vs = _token_stride(v, Hkv, p["v_head_dim"]) if v_out is not None else 0
     q_out = torch.empty((q.shape[0], H, d), dtype=q.dtype, device=q.device) if q_out is None else q_out
     k_out = torch.empty((k.shape[0], Hkv, d), dtype=k.dtype, device=k.device) if k_out is None \
         else k_out
-    for name, x, kv in (("q_out", q_out, False), ("k_out", k_out, True)) + (
-            (("v_out", v_out, True),) if v_out is not None else ()):
+    for name, x, kv in (("q_out", q_out, False), ("k_out", k_out, True)):
         _need(plan, x, name, kv=kv)
+    if v_out is not None:
+        _need(plan, v_out, "v_out", kv=True, vd=True)
     _check("rope_qkv", load_library().rope_qkv(
         plan.handle, q.data_ptr(), qs, k.data_ptr(), ks,
         v.data_ptr() if v_out is not None else None, vs, q_out.data_ptr(), k_out.data_ptr(),
@@ -244,12 +250,14 @@ def rope_qkv_fp8(plan: Plan, q, k, v, scales, q_out=None, k_out=None, v_out=None
         _need(plan, x, name, torch.uint8, dense=False)
         codes.append(x)
     q, k, v = codes
-    qs, ks, vs = _token_stride(q, H, d), _token_stride(k, Hkv, d), _token_stride(v, Hkv, d)
-    mk = lambda t, heads: torch.empty((q.shape[0], heads, d), dtype=torch.bfloat16,
-                                      device=q.device) if t is None else t
-    q_out, k_out, v_out = mk(q_out, H), mk(k_out, Hkv), mk(v_out, Hkv)
-    for name, x, kv in (("q_out", q_out, False), ("k_out", k_out, True), ("v_out", v_out, True)):
-        _need(plan, x, name, kv=kv)
+    dv = p["v_head_dim"]
+    qs, ks, vs = _token_stride(q, H, d), _token_stride(k, Hkv, d), _token_stride(v, Hkv, dv)
+    mk = lambda t, heads, w: torch.empty((q.shape[0], heads, w), dtype=torch.bfloat16,
+                                         device=q.device) if t is None else t
+    q_out, k_out, v_out = mk(q_out, H, d), mk(k_out, Hkv, d), mk(v_out, Hkv, dv)
+    for name, x, kv, vd in (("q_out", q_out, False, False), ("k_out", k_out, True, False),
+                            ("v_out", v_out, True, True)):
+        _need(plan, x, name, kv=kv, vd=vd)
     sc = (ctypes.c_float * 3)(*[float(x) for x in scales])
     _check("rope_qkv_fp8", load_library().rope_qkv_fp8(
         plan.handle, q.data_ptr(), qs, k.data_ptr(), ks, v.data_ptr(), vs, sc,
@@ -268,13 +276,15 @@ def rope_qkv_bwd(plan: Plan, d_q, d_k, q=None, k=None, d_v=None, dq_out=None, dk
     _need(plan, d_q, "d_q", torch.float32)
     _need(plan, d_k, "d_k", torch.float32, kv=True)
     if d_v is not None:
-        _need(plan, d_v, "d_v", torch.float32, kv=True)
+        _need(plan, d_v, "d_v", torch.float32, kv=True, vd=True)
     dq_out = torch.empty_like(d_q) if dq_out is None else dq_out
     dk_out = torch.empty_like(d_k) if dk_out is None else dk_out
     if d_v is not None and dv_out is None:
         dv_out = torch.empty_like(d_v)
     _need(plan, dq_out, "dq_out", torch.float32)
     _need(plan, dk_out, "dk_out", torch.float32, kv=True)
+    if d_v is not None:
+        _need(plan, dv_out, "dv_out", torch.float32, kv=True, vd=True)
     qs = ks = 0
     if p["qk_norm"]:
         if q is None or k is None:
@@ -291,14 +301,15 @@ def rope_qkv_bwd(plan: Plan, d_q, d_k, q=None, k=None, d_v=None, dq_out=None, dk
 
 
 def attn_fwd(plan: Plan, q, k, v, o=None, lse=None):
-    """O [N, H, d] (plan dtype) and LSE float32 [H', N']."""
-    for name, x, kv in (("q", q, False), ("k", k, True), ("v", v, True)):
-        _need(plan, x, name, kv=kv)
+    """O [N, H, dv] (plan dtype) and LSE float32 [H', N']."""
+    for name, x, kv, vd in (("q", q, False, False), ("k", k, True, False), ("v", v, True, True)):
+        _need(plan, x, name, kv=kv, vd=vd)
     info = plan.info
-    o = torch.empty_like(q) if o is None else o
+    o = torch.empty((q.shape[0], q.shape[1], v.shape[2]), dtype=q.dtype, device=q.device) \
+        if o is None else o
     lse = torch.empty((info["attn_heads"], info["slots"]), dtype=torch.float32,
                       device=q.device) if lse is None else lse
-    _need(plan, o, "o")
+    _need(plan, o, "o", vd=True)
     _need(plan, lse, "lse", torch.float32, dense=False)
     if tuple(lse.shape) != (info["attn_heads"], info["slots"]) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous float32 [H', N']")
@@ -309,17 +320,18 @@ def attn_fwd(plan: Plan, q, k, v, o=None, lse=None):
 
 
 def attn_bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None):
-    """dQ float32 [N, H, d]; dK, dV float32 [N, Hkv, d] (gradients with respect to
-    the rotated q, k and v)."""
-    for name, x, kv in (("q", q, False), ("k", k, True), ("v", v, True), ("o", o, False),
-                        ("do", do, False)):
-        _need(plan, x, name, kv=kv)
+    """dQ float32 [N, H, d]; dK float32 [N, Hkv, d], dV float32 [N, Hkv, dv] (gradients
+    with respect to the rotated q, k and v)."""
+    for name, x, kv, vd in (("q", q, False, False), ("k", k, True, False), ("v", v, True, True),
+                            ("o", o, False, True), ("do", do, False, True)):
+        _need(plan, x, name, kv=kv, vd=vd)
     _need(plan, lse, "lse", torch.float32, dense=False)
     mk = lambda t, ref: torch.empty(ref.shape, dtype=torch.float32, device=q.device) \
         if t is None else t
     dq, dk, dv = mk(dq, q), mk(dk, k), mk(dv, v)
-    for name, x, kv in (("dq", dq, False), ("dk", dk, True), ("dv", dv, True)):
-        _need(plan, x, name, torch.float32, kv=kv)
+    for name, x, kv, vd in (("dq", dq, False, False), ("dk", dk, True, False),
+                            ("dv", dv, True, True)):
+        _need(plan, x, name, torch.float32, kv=kv, vd=vd)
     _check("attn_bwd", load_library().attn_bwd(plan.handle, q.data_ptr(), k.data_ptr(),
                                                v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                                do.data_ptr(), dq.data_ptr(), dk.data_ptr(),

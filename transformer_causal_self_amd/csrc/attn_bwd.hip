@@ -120,72 +120,87 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const __bf16 *p) {
   return *reinterpret_cast<const bf16x8 *>(p);
 }
 
-template <int D>
+// two blocks per CU only when both widths are 64 (registers and LDS allow it)
+template <int D, int DV>
 constexpr int bwd_min_blocks() {
-  return D == 64 ? 2 : 1;
+  return D == 64 && DV == 64 ? 2 : 1;
 }
 
 // ---------------------------------------------------------------- dK, dV --
 
-template <int D>
+// D: width of Q, K (and their gradients); DV: width of V, O, dO, dV.
+template <int D, int DV>
 struct DkvBuf {
-  static constexpr int RS = D + 8, TS = 72, BQ = kBwdBQ;
+  static constexpr int RS = D + 8, RSV = DV + 8, TS = 72, BQ = kBwdBQ;
   __bf16 q[BQ * RS];
-  __bf16 g[BQ * RS];
+  __bf16 g[BQ * RSV];
   __bf16 qt[D * TS];
-  __bf16 gt[D * TS];
+  __bf16 gt[DV * TS];
   float lse2[BQ];  // LSE * log2(e)
   float dl[BQ];    // -D (the start value of the dP accumulator)
 };
-template <int D>
+template <int D, int DV>
 struct DkvSmem {
-  static constexpr int RS = DkvBuf<D>::RS, TS = DkvBuf<D>::TS;
-  DkvBuf<D> b[2];  // double buffered: one barrier per query tile
+  DkvBuf<D, DV> b[2];  // double buffered: one barrier per query tile
 };
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dkv_kernel(
+template <int D, int DV, int NW>
+__global__ __launch_bounds__(64 * NW, (bwd_min_blocks<D, DV>())) void dkv_kernel(
     const WorkItem *__restrict__ items, const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const __bf16 *__restrict__ V, const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
     const float *__restrict__ delta, float *__restrict__ dK, float *__restrict__ dV, int Hs,
     int Hks, int G, int64_t Ns, float scale, float scale_log2, int causal, int window) {
-  constexpr int RS = DkvSmem<D>::RS, TS = DkvSmem<D>::TS, BQ = kBwdBQ;
-  __shared__ __attribute__((aligned(16))) DkvSmem<D> sm;
+  constexpr int RS = DkvBuf<D, DV>::RS, RSV = DkvBuf<D, DV>::RSV, TS = DkvBuf<D, DV>::TS;
+  constexpr int BQ = kBwdBQ;
+  __shared__ __attribute__((aligned(16))) DkvSmem<D, DV> sm;
   const WorkItem it = items[blockIdx.x];  // keys [q0, q1), queries [k0, k1)
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int h = lane >> 5, l32 = lane & 31;
   // the item's head is a query head; with grouped K/V heads (G > 1) its
   // K/V head is it.head / G, and the group's items add into dK and dV
-  const int64_t rs = (int64_t)Hs * D;    // Q / dO elements between consecutive slots
-  const int64_t rsk = (int64_t)Hks * D;  // K / V / dK / dV
-  const int64_t ho = (int64_t)it.head * D;
-  const int64_t hk = (int64_t)(it.head / G) * D;
+  const int64_t rs = (int64_t)Hs * D;     // Q elements between consecutive slots
+  const int64_t rso = (int64_t)Hs * DV;   // dO
+  const int64_t rsk = (int64_t)Hks * D;   // K / dK
+  const int64_t rsv = (int64_t)Hks * DV;  // V / dV
+  const int64_t ho = (int64_t)it.head * D, hoo = (int64_t)it.head * DV;
+  const int64_t hk = (int64_t)(it.head / G) * D, hv = (int64_t)(it.head / G) * DV;
   const int wk0 = it.q0 + 32 * w, wk1 = min(wk0 + 32, it.q1);
   const int kj = wk0 + l32;  // this lane's key (column of S)
   const bool kok = kj < it.q1;
 
-  bf16x8 kf[D / 16], vf[D / 16];
+  bf16x8 kf[D / 16], vf[DV / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
     if (kok) {
       kf[c] = load_bf16x8(K + hk + kj * rsk + 16 * c + 8 * h);
-      vf[c] = load_bf16x8(V + hk + kj * rsk + 16 * c + 8 * h);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kf[c][e] = vf[c][e] = (__bf16)0.0f;
+      for (int e = 0; e < 8; ++e) kf[c][e] = (__bf16)0.0f;
     }
   }
-  floatx16 dv[D / 32], dk[D / 32];
 #pragma unroll
-  for (int dl = 0; dl < D / 32; ++dl) dv[dl] = dk[dl] = floatx16{};
+  for (int c = 0; c < DV / 16; ++c) {
+    if (kok) {
+      vf[c] = load_bf16x8(V + hv + kj * rsv + 16 * c + 8 * h);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vf[c][e] = (__bf16)0.0f;
+    }
+  }
+  floatx16 dv[DV / 32], dk[D / 32];
+#pragma unroll
+  for (int dl = 0; dl < DV / 32; ++dl) dv[dl] = floatx16{};
+#pragma unroll
+  for (int dl = 0; dl < D / 32; ++dl) dk[dl] = floatx16{};
 
   const int nq = (it.k1 - it.k0 + BQ - 1) / BQ;
-  PairStage<D, 64 * NW> sq, sg;
+  PairStage<D, 64 * NW> sq;
+  PairStage<DV, 64 * NW> sg;
   float st_lse = 0.0f;
   auto load_tile = [&](int q0) {
     sq.load(Q + ho, rs, q0, it.k1, tid);
-    sg.load(dO + ho, rs, q0, it.k1, tid);
+    sg.load(dO + hoo, rso, q0, it.k1, tid);
     if (tid < 2 * BQ) {
       const int row = q0 + (tid % BQ);
       st_lse = row < it.k1 ? (tid < BQ ? LSE[(int64_t)it.head * Ns + row] * kLog2e
@@ -193,7 +208,7 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dkv_kernel(
                            : 0.0f;
     }
   };
-  auto store_tile = [&](DkvBuf<D> &bf) {
+  auto store_tile = [&](DkvBuf<D, DV> &bf) {
     sq.store(bf.q, bf.qt, tid);
     sg.store(bf.g, bf.gt, tid);
     if (tid < BQ) bf.lse2[tid] = st_lse;
@@ -205,7 +220,7 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dkv_kernel(
   __syncthreads();
   for (int t = 0; t < nq; ++t) {
     const int qt0 = it.k0 + t * BQ;
-    const DkvBuf<D> &cur = sm.b[t & 1];
+    const DkvBuf<D, DV> &cur = sm.b[t & 1];
     const int qt1 = min(qt0 + BQ, it.k1);  // one past the last valid query
     const bool active = wk0 < wk1 && !(causal && qt1 - 1 < wk0) &&
                         !(window > 0 && qt0 - (wk1 - 1) >= window);
@@ -234,8 +249,8 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dkv_kernel(
       for (int c = 0; c < D / 16; ++c)
         s = mfma32x32x16(load_bf16x8(&cur.q[(32 * rho + l32) * RS + 16 * c + 8 * h]), kf[c], s);
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c)
-        dp = mfma32x32x16(load_bf16x8(&cur.g[(32 * rho + l32) * RS + 16 * c + 8 * h]), vf[c], dp);
+      for (int c = 0; c < DV / 16; ++c)
+        dp = mfma32x32x16(load_bf16x8(&cur.g[(32 * rho + l32) * RSV + 16 * c + 8 * h]), vf[c], dp);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const float4 l4 = *reinterpret_cast<const float4 *>(&cur.lse2[32 * rho + 8 * b + 4 * h]);
@@ -255,12 +270,12 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dkv_kernel(
       const bf16x8 pa[2] = {to_bf16x8(s, 0), to_bf16x8(s, 8)};
       const bf16x8 da[2] = {to_bf16x8(dp, 0), to_bf16x8(dp, 8)};
 #pragma unroll
-      for (int dl = 0; dl < D / 32; ++dl)
+      for (int dl = 0; dl < (D > DV ? D : DV) / 32; ++dl)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           const int off = (32 * dl + l32) * TS + 32 * rho + 16 * m + 8 * h;
-          dv[dl] = mfma32x32x16(pa[m], load_bf16x8(&cur.gt[off]), dv[dl]);
-          dk[dl] = mfma32x32x16(da[m], load_bf16x8(&cur.qt[off]), dk[dl]);
+          if (dl < DV / 32) dv[dl] = mfma32x32x16(pa[m], load_bf16x8(&cur.gt[off]), dv[dl]);
+          if (dl < D / 32) dk[dl] = mfma32x32x16(da[m], load_bf16x8(&cur.qt[off]), dk[dl]);
         }
     }
     }
@@ -275,16 +290,19 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dkv_kernel(
   for (int r = 0; r < 16; ++r) {
     const int key = wk0 + 8 * (r / 4) + 4 * h + (r % 4);
     if (key < it.q1) {
+      // with grouped heads, the group's query heads share this K/V row
+      // (zeroed first) and add into it
+#pragma unroll
+      for (int dl = 0; dl < DV / 32; ++dl) {
+        const int64_t off = key * rsv + hv + 32 * dl + l32;
+        if (G == 1) dV[off] = dv[dl][r];
+        else unsafeAtomicAdd(&dV[off], dv[dl][r]);
+      }
 #pragma unroll
       for (int dl = 0; dl < D / 32; ++dl) {
         const int64_t off = key * rsk + hk + 32 * dl + l32;
-        if (G == 1) {
-          dV[off] = dv[dl][r];
-          dK[off] = dk[dl][r] * scale;
-        } else {  // the group's query heads share this K/V row (zeroed first)
-          unsafeAtomicAdd(&dV[off], dv[dl][r]);
-          unsafeAtomicAdd(&dK[off], dk[dl][r] * scale);
-        }
+        if (G == 1) dK[off] = dk[dl][r] * scale;
+        else unsafeAtomicAdd(&dK[off], dk[dl][r] * scale);
       }
     }
   }
@@ -292,49 +310,60 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dkv_kernel(
 
 // -------------------------------------------------------------------- dQ --
 
-template <int D>
+template <int D, int DV>
 struct DqBuf {
-  static constexpr int RS = D + 8, TS = 72;
+  static constexpr int RS = D + 8, RSV = DV + 8, TS = 72;
   __bf16 k[kFwdBK * RS];
-  __bf16 v[kFwdBK * RS];
+  __bf16 v[kFwdBK * RSV];
   __bf16 kt[D * TS];
 };
-template <int D>
+template <int D, int DV>
 struct DqSmem {
-  static constexpr int RS = DqBuf<D>::RS, TS = DqBuf<D>::TS;
-  DqBuf<D> b[2];  // double buffered: one barrier per key tile
+  DqBuf<D, DV> b[2];  // double buffered: one barrier per key tile
 };
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dq_kernel(
+template <int D, int DV, int NW>
+__global__ __launch_bounds__(64 * NW, (bwd_min_blocks<D, DV>())) void dq_kernel(
     const WorkItem *__restrict__ items, const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const __bf16 *__restrict__ V, const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
     const float *__restrict__ delta, float *__restrict__ dQ, int Hs, int Hks, int G, int64_t Ns,
     float scale,
     float scale_log2, int causal, int window) {
-  constexpr int RS = DqSmem<D>::RS, TS = DqSmem<D>::TS, BK = kFwdBK;
-  __shared__ __attribute__((aligned(16))) DqSmem<D> sm;
+  constexpr int RS = DqBuf<D, DV>::RS, RSV = DqBuf<D, DV>::RSV, TS = DqBuf<D, DV>::TS;
+  constexpr int BK = kFwdBK;
+  __shared__ __attribute__((aligned(16))) DqSmem<D, DV> sm;
   const WorkItem it = items[blockIdx.x];  // queries [q0, q1), keys [k0, k1)
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int h = lane >> 5, l32 = lane & 31;
-  const int64_t rs = (int64_t)Hs * D;    // Q / dO / dQ elements between consecutive slots
-  const int64_t rsk = (int64_t)Hks * D;  // K / V
-  const int64_t ho = (int64_t)it.head * D;
-  const int64_t hk = (int64_t)(it.head / G) * D;  // the query head's K/V head
+  const int64_t rs = (int64_t)Hs * D;     // Q / dQ elements between consecutive slots
+  const int64_t rso = (int64_t)Hs * DV;   // dO
+  const int64_t rsk = (int64_t)Hks * D;   // K
+  const int64_t rsv = (int64_t)Hks * DV;  // V
+  const int64_t ho = (int64_t)it.head * D, hoo = (int64_t)it.head * DV;
+  // the query head's K/V head
+  const int64_t hk = (int64_t)(it.head / G) * D, hv = (int64_t)(it.head / G) * DV;
   const int wq0 = it.q0 + 32 * w, wq1 = min(wq0 + 32, it.q1);
   const int qi = wq0 + l32;
   const bool qok = qi < it.q1;
 
-  bf16x8 qf[D / 16], gf[D / 16];
+  bf16x8 qf[D / 16], gf[DV / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
     if (qok) {
       qf[c] = load_bf16x8(Q + ho + qi * rs + 16 * c + 8 * h);
-      gf[c] = load_bf16x8(dO + ho + qi * rs + 16 * c + 8 * h);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qf[c][e] = gf[c][e] = (__bf16)0.0f;
+      for (int e = 0; e < 8; ++e) qf[c][e] = (__bf16)0.0f;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < DV / 16; ++c) {
+    if (qok) {
+      gf[c] = load_bf16x8(dO + hoo + qi * rso + 16 * c + 8 * h);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gf[c][e] = (__bf16)0.0f;
     }
   }
   const float lse2 = qok ? LSE[(int64_t)it.head * Ns + qi] * kLog2e : 0.0f;
@@ -351,19 +380,20 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dq_kernel(
   for (int dl = 0; dl < D / 32; ++dl) dq[dl] = floatx16{};
 
   const int nk = (it.k1 - it.k0 + BK - 1) / BK;
-  PairStage<D, 64 * NW> sk, sv;
+  PairStage<D, 64 * NW> sk;
+  PairStage<DV, 64 * NW> sv;
   sk.load(K + hk, rsk, it.k0, it.k1, tid);
-  sv.load(V + hk, rsk, it.k0, it.k1, tid);
+  sv.load(V + hv, rsv, it.k0, it.k1, tid);
   sk.store(sm.b[0].k, sm.b[0].kt, tid);
   sv.store(sm.b[0].v, nullptr, tid);
   if (nk > 1) {
     sk.load(K + hk, rsk, it.k0 + BK, it.k1, tid);
-    sv.load(V + hk, rsk, it.k0 + BK, it.k1, tid);
+    sv.load(V + hv, rsv, it.k0 + BK, it.k1, tid);
   }
   __syncthreads();
   for (int t = 0; t < nk; ++t) {
     const int kt0 = it.k0 + t * BK;
-    const DqBuf<D> &cur = sm.b[t & 1];
+    const DqBuf<D, DV> &cur = sm.b[t & 1];
     const bool active = wq0 < wq1 && !(causal && kt0 > wq1 - 1) &&
                         !(window > 0 && wq0 - (kt0 + BK - 1) >= window);
     if (active) {
@@ -384,8 +414,8 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dq_kernel(
         s[beta] = mfma32x32x16(load_bf16x8(&cur.k[(32 * beta + l32) * RS + 16 * c + 8 * h]), qf[c],
                                s[beta]);
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c)
-        dp[beta] = mfma32x32x16(load_bf16x8(&cur.v[(32 * beta + l32) * RS + 16 * c + 8 * h]),
+      for (int c = 0; c < DV / 16; ++c)
+        dp[beta] = mfma32x32x16(load_bf16x8(&cur.v[(32 * beta + l32) * RSV + 16 * c + 8 * h]),
                                 gf[c], dp[beta]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[beta][r] = fast_exp2(fmaf(s[beta][r], scale_log2, -lse2));
@@ -414,7 +444,7 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dq_kernel(
       sv.store(sm.b[(t + 1) & 1].v, nullptr, tid);
       if (t + 2 < nk) {
         sk.load(K + hk, rsk, kt0 + 2 * BK, it.k1, tid);
-        sv.load(V + hk, rsk, kt0 + 2 * BK, it.k1, tid);
+        sv.load(V + hv, rsv, kt0 + 2 * BK, it.k1, tid);
       }
     }
     __syncthreads();
@@ -431,18 +461,17 @@ __global__ __launch_bounds__(64 * NW, bwd_min_blocks<D>()) void dq_kernel(
   }
 }
 
-// Zero n floats (dK and dV before the grouped heads add into them; a kernel
-// rather than a memset, so the launch sequence stays graph-capturable).
-__global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ a, float *__restrict__ b,
-                                                   int64_t n) {
+// Zero na floats of a and nb of b (dK and dV before the grouped heads add
+// into them; a kernel rather than a memset, so the launch sequence stays
+// graph-capturable).
+__global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ a, int64_t na,
+                                                   float *__restrict__ b, int64_t nb) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) {
-    a[i] = 0.0f;
-    b[i] = 0.0f;
-  }
+  if (i < na) a[i] = 0.0f;
+  if (i < nb) b[i] = 0.0f;
 }
 
-template <int D>
+template <int D, int DV = D>
 hipError_t launch_typed(const attn_plan *p, const void *q, const void *k, const void *v,
                         const void *o, const float *lse, const void *d_o, float *dq, float *dk,
                         float *dv, hipStream_t stream) {
@@ -455,20 +484,21 @@ hipError_t launch_typed(const attn_plan *p, const void *q, const void *k, const 
   const __bf16 *G = static_cast<const __bf16 *>(d_o);
   const int64_t rows = Ns * Hs;
   constexpr int NWK = kBwdWaves, NWQ = kBwdWaves;
-  hipLaunchKernelGGL((delta_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
-                     O, G, delta, Hs, Ns);
+  hipLaunchKernelGGL((delta_kernel<DV>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                     stream, O, G, delta, Hs, Ns);
   if (p->p.G > 1) {
-    const int64_t n = p->p.Ns * p->p.Hks * D;
+    const int64_t nk = p->p.Ns * p->p.Hks * D, nv = p->p.Ns * p->p.Hks * DV;
+    const int64_t n = nk > nv ? nk : nv;
     hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, dk,
-                       dv, n);
+                       nk, dv, nv);
   }
   if (!p->bwd.empty())
-    hipLaunchKernelGGL((dkv_kernel<D, NWK>), dim3((unsigned)p->bwd.size()), dim3(64 * NWK), 0,
+    hipLaunchKernelGGL((dkv_kernel<D, DV, NWK>), dim3((unsigned)p->bwd.size()), dim3(64 * NWK), 0,
                        stream, reinterpret_cast<const WorkItem *>(p->ws + p->off_bwd), Q, K, V, G,
                        lse, delta, dk, dv, Hs, p->p.Hks, p->p.G, Ns, scale, scale_log2,
                        p->p.causal, p->p.window);
   if (!p->dq.empty())
-    hipLaunchKernelGGL((dq_kernel<D, NWQ>), dim3((unsigned)p->dq.size()), dim3(64 * NWQ), 0,
+    hipLaunchKernelGGL((dq_kernel<D, DV, NWQ>), dim3((unsigned)p->dq.size()), dim3(64 * NWQ), 0,
                        stream, reinterpret_cast<const WorkItem *>(p->ws + p->off_dq), Q, K, V, G,
                        lse, delta, dq, Hs, p->p.Hks, p->p.G, Ns, scale, scale_log2,
                        p->p.causal, p->p.window);
@@ -480,8 +510,12 @@ hipError_t launch_typed(const attn_plan *p, const void *q, const void *k, const 
 attn_status launch_bwd(const attn_plan *p, const void *q, const void *k, const void *v,
                        const void *o, const float *lse, const void *d_o, float *dq, float *dk,
                        float *dv, hipStream_t stream) {
-  const hipError_t e = p->p.d == 64 ? launch_typed<64>(p, q, k, v, o, lse, d_o, dq, dk, dv, stream)
-                                    : launch_typed<128>(p, q, k, v, o, lse, d_o, dq, dk, dv, stream);
+  const int d = p->p.d, w = p->p.dv;
+  hipError_t e;
+  if (d == 64 && w == 64) e = launch_typed<64>(p, q, k, v, o, lse, d_o, dq, dk, dv, stream);
+  else if (d == 64) e = launch_typed<64, 128>(p, q, k, v, o, lse, d_o, dq, dk, dv, stream);
+  else if (w == 64) e = launch_typed<128, 64>(p, q, k, v, o, lse, d_o, dq, dk, dv, stream);
+  else e = launch_typed<128>(p, q, k, v, o, lse, d_o, dq, dk, dv, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 

@@ -264,29 +264,31 @@ __global__ __launch_bounds__(kFwdThreadsF32, fwd_min_blocks<T>()) void fwd_kerne
 // tile max exceeds it by more than 2^8 in the exp2 domain (the weights stay
 // below 256, so nothing overflows, and O / l is unchanged).
 
-template <int D>
+// D: width of Q and K rows; DV: width of V and O rows.
+template <int D, int DV>
 struct SmemBF {
   static constexpr int KS = D + 8;   // K row stride (elements): 16-byte rows, 4-bank shift
   static constexpr int VS = BK + 8;  // V^T row stride (elements)
   __bf16 k[2][BK * KS];
-  __bf16 vt[2][D * VS];
+  __bf16 vt[2][DV * VS];
 };
 
-template <int D, int NT>
+template <int D, int DV, int NT>
 struct StageBF {
   static constexpr int KPT = BK * D / 8 / NT;  // 16-byte K chunks per thread
   static_assert(KPT >= 1 && BK * D / 8 % NT == 0, "K staging split");
-  static constexpr int VU = (BK / 2) * (D / 8);  // (key pair, 8 features) units per tile
+  static constexpr int VU = (BK / 2) * (DV / 8);  // (key pair, 8 features) units per tile
   static constexpr int VPT = (VU + NT - 1) / NT;
   uint4 kr[KPT];
   uint4 vr[VPT][2];
 
-  // Rows [kt0, kt0 + BK) of the head's K and V; rows past `rows` read zero.
+  // Rows [kt0, kt0 + BK) of the head's K and V (row strides rsb, rsbv bytes);
+  // rows past `rows` read zero.
   __device__ __forceinline__ void load(const __bf16 *Kt, const __bf16 *Vt, int rows, uint32_t rsb,
-                                       int tid) {
-    const uint32_t bytes = (uint32_t)max(0, min(rows, BK)) * rsb;
-    const auto rk = make_rsrc(Kt, bytes);
-    const auto rv = make_rsrc(Vt, bytes);
+                                       uint32_t rsbv, int tid) {
+    const uint32_t nr = (uint32_t)max(0, min(rows, BK));
+    const auto rk = make_rsrc(Kt, nr * rsb);
+    const auto rv = make_rsrc(Vt, nr * rsbv);
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int ci = tid + NT * r;
@@ -296,14 +298,14 @@ struct StageBF {
     for (int r = 0; r < VPT; ++r) {
       const int vi = tid + NT * r;
       if (VU % NT != 0 && vi >= VU) break;
-      const uint32_t off = (uint32_t)(2 * (vi % (BK / 2))) * rsb + 16u * (vi / (BK / 2));
+      const uint32_t off = (uint32_t)(2 * (vi % (BK / 2))) * rsbv + 16u * (vi / (BK / 2));
       vr[r][0] = buf_load16(rv, off);
-      vr[r][1] = buf_load16(rv, off + rsb);
+      vr[r][1] = buf_load16(rv, off + rsbv);
     }
   }
 
   __device__ __forceinline__ void store(__bf16 *kdst, __bf16 *vtdst, int tid) const {
-    constexpr int KS = SmemBF<D>::KS, VS = SmemBF<D>::VS;
+    constexpr int KS = SmemBF<D, DV>::KS, VS = SmemBF<D, DV>::VS;
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int ci = tid + NT * r;
@@ -362,22 +364,24 @@ __device__ __forceinline__ void scores_again(const __bf16 *ks, const bf16x8 (&qf
 }
 
 // NW waves (32 query slots each) per work item.
-template <int D, int NW>
+template <int D, int DV, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
     const WorkItem *__restrict__ items, const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const __bf16 *__restrict__ V, __bf16 *__restrict__ O, float *__restrict__ LSE, int Hs,
     int Hks, int G, int64_t Ns, float scale, float scale_log2, int causal, int window) {
-  constexpr int KS = SmemBF<D>::KS, VS = SmemBF<D>::VS;
-  __shared__ __attribute__((aligned(16))) SmemBF<D> sm;
+  constexpr int KS = SmemBF<D, DV>::KS, VS = SmemBF<D, DV>::VS;
+  __shared__ __attribute__((aligned(16))) SmemBF<D, DV> sm;
   const WorkItem it = items[blockIdx.x];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int h = lane >> 5, l32 = lane & 31;
-  const int64_t rs = (int64_t)Hs * D;    // Q / O elements between consecutive slots
-  const int64_t rsk = (int64_t)Hks * D;  // K / V elements between consecutive slots
-  const uint32_t rsbq = (uint32_t)rs * 2u, rsb = (uint32_t)rsk * 2u;
+  const int64_t rs = (int64_t)Hs * D;     // Q elements between consecutive slots
+  const int64_t rso = (int64_t)Hs * DV;   // O
+  const int64_t rsk = (int64_t)Hks * D;   // K
+  const int64_t rsv = (int64_t)Hks * DV;  // V
+  const uint32_t rsbq = (uint32_t)rs * 2u, rsb = (uint32_t)rsk * 2u, rsbv = (uint32_t)rsv * 2u;
   const __bf16 *Kh = K + (int64_t)(it.head / G) * D;  // the query head's K/V head
-  const __bf16 *Vh = V + (int64_t)(it.head / G) * D;
+  const __bf16 *Vh = V + (int64_t)(it.head / G) * DV;
 
   const int wq0 = it.q0 + 32 * w;       // first query of this wave
   const int wq1 = min(wq0 + 32, it.q1);  // one past its last valid query
@@ -394,9 +398,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
       qf[c] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)l32 * rsbq + 32u * c + 16u * h));
   }
 
-  floatx16 o[D / 32];
+  floatx16 o[DV / 32];
 #pragma unroll
-  for (int dl = 0; dl < D / 32; ++dl) o[dl] = floatx16{};
+  for (int dl = 0; dl < DV / 32; ++dl) o[dl] = floatx16{};
   float m = kMinusBig;  // running max of raw scores (the exponent's reference)
   float mb = m * scale_log2;
   float l = 0.0f;       // this lane's part of the running sum
@@ -404,12 +408,12 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
 
   const int nk = (it.k1 - it.k0 + BK - 1) / BK;
   constexpr int NT = 64 * NW;
-  StageBF<D, NT> st;
-  st.load(Kh + (int64_t)it.k0 * rsk, Vh + (int64_t)it.k0 * rsk, it.k1 - it.k0, rsb, tid);
+  StageBF<D, DV, NT> st;
+  st.load(Kh + (int64_t)it.k0 * rsk, Vh + (int64_t)it.k0 * rsv, it.k1 - it.k0, rsb, rsbv, tid);
   st.store(sm.k[0], sm.vt[0], tid);
   if (nk > 1)
-    st.load(Kh + (int64_t)(it.k0 + BK) * rsk, Vh + (int64_t)(it.k0 + BK) * rsk,
-            it.k1 - it.k0 - BK, rsb, tid);
+    st.load(Kh + (int64_t)(it.k0 + BK) * rsk, Vh + (int64_t)(it.k0 + BK) * rsv,
+            it.k1 - it.k0 - BK, rsb, rsbv, tid);
   __syncthreads();
 
   for (int t = 0; t < nk; ++t) {
@@ -470,7 +474,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
         mb = m_new * scale_log2;
         l *= alpha;
 #pragma unroll
-        for (int dl = 0; dl < D / 32; ++dl)
+        for (int dl = 0; dl < DV / 32; ++dl)
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[dl][r] *= alpha;
         ls = 0.0f;
@@ -497,7 +501,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-          for (int dl = 0; dl < D / 32; ++dl) {
+          for (int dl = 0; dl < DV / 32; ++dl) {
             const bf16x8 va = *reinterpret_cast<const bf16x8 *>(
                 &vts[(32 * dl + l32) * VS + 32 * beta + 16 * mm + 8 * h]);
             o[dl] = mfma32x32x16(va, pf[beta][mm], o[dl]);
@@ -506,8 +510,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
     if (t + 1 < nk) {
       st.store(sm.k[buf ^ 1], sm.vt[buf ^ 1], tid);
       if (t + 2 < nk)
-        st.load(Kh + (int64_t)(kt0 + 2 * BK) * rsk, Vh + (int64_t)(kt0 + 2 * BK) * rsk,
-                it.k1 - kt0 - 2 * BK, rsb, tid);
+        st.load(Kh + (int64_t)(kt0 + 2 * BK) * rsk, Vh + (int64_t)(kt0 + 2 * BK) * rsv,
+                it.k1 - kt0 - 2 * BK, rsb, rsbv, tid);
     }
     __syncthreads();
   }
@@ -516,9 +520,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
   const float lt = halves_sum(l);
   if (qok) {
     const float inv = 1.0f / lt;
-    __bf16 *orow = O + (int64_t)qi * rs + (int64_t)it.head * D;
+    __bf16 *orow = O + (int64_t)qi * rso + (int64_t)it.head * DV;
 #pragma unroll
-    for (int dl = 0; dl < D / 32; ++dl)
+    for (int dl = 0; dl < DV / 32; ++dl)
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         float x[4];
@@ -530,9 +534,10 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int DV = D>
 hipError_t launch_typed(const attn_plan *p, const void *q, const void *k, const void *v, void *o,
                         float *lse, hipStream_t stream) {
+  static_assert(std::is_same<T, __bf16>::value || DV == D, "fp32 keeps one head width");
   const WorkItem *items = reinterpret_cast<const WorkItem *>(p->ws + p->off_fwd);
   const unsigned n = (unsigned)p->fwd.size();
   if (n == 0) return hipSuccess;
@@ -540,13 +545,13 @@ hipError_t launch_typed(const attn_plan *p, const void *q, const void *k, const 
   const float scale_log2 = scale * 1.4426950408889634f;
   const Problem &P = p->p;
   if (std::is_same<T, __bf16>::value && p->fwd_bq == kFwdBQ)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, kFwdBQ / 32>), dim3(n), dim3(2 * kFwdBQ), 0, stream,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, kFwdBQ / 32>), dim3(n), dim3(2 * kFwdBQ), 0, stream,
                        items, static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
                        static_cast<const __bf16 *>(v), static_cast<__bf16 *>(o), lse, P.Hs, P.Hks,
                        P.G, P.Ns, scale, scale_log2, P.causal, P.window);
   else if (std::is_same<T, __bf16>::value)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, kFwdBQShort / 32>), dim3(n), dim3(2 * kFwdBQShort), 0,
-                       stream, items, static_cast<const __bf16 *>(q),
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, kFwdBQShort / 32>), dim3(n),
+                       dim3(2 * kFwdBQShort), 0, stream, items, static_cast<const __bf16 *>(q),
                        static_cast<const __bf16 *>(k), static_cast<const __bf16 *>(v),
                        static_cast<__bf16 *>(o), lse, P.Hs, P.Hks, P.G, P.Ns, scale, scale_log2,
                        P.causal, P.window);
@@ -564,7 +569,12 @@ attn_status launch_fwd(const attn_plan *p, const void *q, const void *k, const v
                        float *lse, hipStream_t stream) {
   hipError_t e;
   const bool bf = p->p.dtype == ATTN_BF16;
-  if (p->p.d == 64)
+  const int d = p->p.d, dv = p->p.dv;  // the plan admits dv != d for bf16 only
+  if (bf && d == 64 && dv == 128)
+    e = launch_typed<__bf16, 64, 128>(p, q, k, v, o, lse, stream);
+  else if (bf && d == 128 && dv == 64)
+    e = launch_typed<__bf16, 128, 64>(p, q, k, v, o, lse, stream);
+  else if (d == 64)
     e = bf ? launch_typed<__bf16, 64>(p, q, k, v, o, lse, stream)
            : launch_typed<float, 64>(p, q, k, v, o, lse, stream);
   else

@@ -63,6 +63,7 @@ struct Problem {
   int32_t G;       // query heads per K/V head: Hs / Hks
   int32_t qk_norm; // RMS-norm of Q and K rows before the rotation
   float norm_eps;
+  int32_t dv;      // V / O / dO / dV head dim (= d unless set apart)
 };
 
 }  // namespace attn

@@ -175,6 +175,10 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
   const int Hkv = pr->num_kv_heads == 0 ? pr->num_heads : pr->num_kv_heads;
   if (Hkv < 1 || pr->num_heads % Hkv) return ATTN_E_INVALID;
   if (pr->head_dim != 64 && pr->head_dim != 128) return ATTN_E_UNSUPPORTED;
+  const int dv = pr->v_head_dim == 0 ? pr->head_dim : pr->v_head_dim;
+  if (dv <= 0 || (dv % 2)) return ATTN_E_INVALID;
+  if (dv != 64 && dv != 128) return ATTN_E_UNSUPPORTED;
+  if (dv != pr->head_dim && pr->dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
   if (Hkv != pr->num_heads && pr->paired) return ATTN_E_UNSUPPORTED;
 
   attn_plan *p = new (std::nothrow) attn_plan();
@@ -184,6 +188,7 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
     P.N = pr->num_tokens;
     P.H = pr->num_heads;
     P.d = pr->head_dim;
+    P.dv = dv;
     P.dtype = pr->dtype;
     P.causal = pr->causal;
     P.window = pr->window > 0 ? pr->window : 0;
@@ -269,22 +274,26 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
     order_for_xcds(p->bwd, attn::kBwdBQ, attn::kXcdChunk);
     order_for_xcds(p->dq, attn::kFwdBK, attn::kXcdChunk);
 
-    const double elems = (double)P.N * P.H * P.d;      // Q, O, dO, dQ
-    const double kv_elems = (double)P.N * P.Hkv * P.d;  // K, V, dK, dV
+    const double elems = (double)P.N * P.H * P.d;       // Q, dQ
+    const double kv_elems = (double)P.N * P.Hkv * P.d;  // K, dK
+    const double o_elems = (double)P.N * P.H * P.dv;    // O, dO
+    const double v_elems = (double)P.N * P.Hkv * P.dv;  // V, dV
     const double es = P.dtype == ATTN_BF16 ? 2.0 : 4.0;
     const double lse_bytes = 4.0 * (double)P.Ns * P.Hs;
     attn_plan_info &I = p->info;
     I.visible_pairs = pairs;
-    I.fwd_flops = 4.0 * P.d * (double)pairs;
-    I.bwd_flops = 2.5 * I.fwd_flops;
+    I.fwd_flops = 2.0 * (P.d + P.dv) * (double)pairs;
+    I.bwd_flops = 2.0 * (3.0 * P.d + 2.0 * P.dv) * (double)pairs;
     I.rope_bytes = 2.0 * (elems + kv_elems) * es;
-    I.fwd_bytes = 2.0 * (elems + kv_elems) * es + lse_bytes;
-    I.bwd_bytes = (3.0 * elems + 2.0 * kv_elems) * es + lse_bytes + (elems + 2.0 * kv_elems) * 4.0;
+    I.fwd_bytes = (elems + kv_elems + v_elems + o_elems) * es + lse_bytes;
+    I.bwd_bytes = (elems + kv_elems + v_elems + 2.0 * o_elems) * es + lse_bytes +
+                  (elems + kv_elems + v_elems) * 4.0;
     I.fwd_items = (int64_t)p->fwd.size();
     I.bwd_items = (int64_t)p->bwd.size();
     I.slots = P.Ns;
     I.attn_heads = P.Hs;
     I.kv_heads = P.Hks;
+    I.v_head_dim = P.dv;
     I.max_positions = p->max_pos;
 
     // Workspace layout.
@@ -368,9 +377,10 @@ attn_status rope_qkv(const attn_plan *p, const void *q, int64_t qs, const void *
   if (!p->ws) return ATTN_E_WORKSPACE;
   const int64_t row = (int64_t)p->p.H * p->p.d;
   const int64_t kv_row = (int64_t)p->p.Hkv * p->p.d;
+  const int64_t v_row = (int64_t)p->p.Hkv * p->p.dv;
   if (p->p.N == 0) return ATTN_OK;
   if (!q || !k || !q_out || !k_out || (v_out && !v)) return ATTN_E_INVALID;
-  if (qs < row || ks < kv_row || (v_out && vs < kv_row)) return ATTN_E_INVALID;
+  if (qs < row || ks < kv_row || (v_out && vs < v_row)) return ATTN_E_INVALID;
   const int64_t vec = p->p.dtype == ATTN_BF16 ? 8 : 4;
   if (qs % vec || ks % vec || (v_out && vs % vec)) return ATTN_E_ALIGN;
   if (!aligned16(q) || !aligned16(k) || !aligned16(q_out) || !aligned16(k_out) ||
@@ -398,8 +408,9 @@ attn_status rope_qkv_fp8(const attn_plan *p, const void *q, int64_t qs, const vo
   if (p->p.N == 0) return ATTN_OK;
   const int64_t row = (int64_t)p->p.H * p->p.d;
   const int64_t kv_row = (int64_t)p->p.Hkv * p->p.d;
+  const int64_t v_row = (int64_t)p->p.Hkv * p->p.dv;
   if (!q || !k || !v || !q_out || !k_out || !v_out) return ATTN_E_INVALID;
-  if (qs < row || ks < kv_row || vs < kv_row) return ATTN_E_INVALID;
+  if (qs < row || ks < kv_row || vs < v_row) return ATTN_E_INVALID;
   // one load covers 8 codes
   const auto a8 = [](const void *x) { return (reinterpret_cast<uintptr_t>(x) & 7) == 0; };
   if (qs % 8 || ks % 8 || vs % 8 || !a8(q) || !a8(k) || !a8(v)) return ATTN_E_ALIGN;

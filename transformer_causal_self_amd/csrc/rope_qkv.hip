@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
     const T *q, int64_t qs, const T *k, int64_t ks, const T *__restrict__ v, int64_t vs, T *qo,
     T *ko, T *__restrict__ vo, const int32_t *__restrict__ tok_pos,
     const float *__restrict__ tcos, const float *__restrict__ tsin, int64_t N, int H, int Hk,
-    float eps) {
+    float eps, int dv) {
   using RC = RopeChunk<T, D, HALF>;
   constexpr int U = RC::U, NP = RC::NP;
   const int64_t gid = (int64_t)blockIdx.x * kRopeThreads + threadIdx.x;
@@ -263,13 +263,13 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
     rotate_heads(q4, qo4, H);
     rotate_heads(k4, ko4, Hk);
   }
-  if (vo) {
+  if (vo) {  // V rows hold dv elements: UV units, spread over the token's U/2 lanes
+    const int UV = dv / RC::V;
     const uint4 *v4 = reinterpret_cast<const uint4 *>(v + n * vs);
-    uint4 *vo4 = reinterpret_cast<uint4 *>(vo + n * (int64_t)Hk * D);
+    uint4 *vo4 = reinterpret_cast<uint4 *>(vo + n * (int64_t)Hk * dv);
     for (int hh = 0; hh < Hk; ++hh) {
-      const int ob = out_head(hh) * U;
-      vo4[ob + c] = v4[hh * U + c];
-      vo4[ob + c + U / 2] = v4[hh * U + c + U / 2];
+      const int ob = out_head(hh) * UV;
+      for (int u = c; u < UV; u += U / 2) vo4[ob + u] = v4[hh * UV + u];
     }
   }
 }
@@ -296,7 +296,8 @@ hipError_t launch_typed(const attn_plan *p, const void *q, int64_t qs, const voi
   const float eps = p->p.norm_eps;
 #define ROPE_LAUNCH(HF, PMV, NRM)                                                          \
   hipLaunchKernelGGL((rope_kernel<T, D, HF, PMV, NRM>), grid, dim3(kRopeThreads), 0, stream, Q, \
-                     qs, K, ks, Vv, vs, QO, KO, VO, pos, tc, ts, N, p->p.H, p->p.Hkv, eps)
+                     qs, K, ks, Vv, vs, QO, KO, VO, pos, tc, ts, N, p->p.H, p->p.Hkv, eps,    \
+                     p->p.dv)
 #define ROPE_PM(HF, NRM)                \
   do {                                  \
     if (pm == 0) ROPE_LAUNCH(HF, 0, NRM); \
@@ -340,7 +341,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_fp8_kernel(
     const uint8_t *__restrict__ v, int64_t vs, __bf16 *__restrict__ qo, __bf16 *__restrict__ ko,
     __bf16 *__restrict__ vo, const int32_t *__restrict__ tok_pos, const float *__restrict__ tcos,
     const float *__restrict__ tsin, int64_t N, int H, int Hk, float eps, float q_scale,
-    float k_scale, float v_scale) {
+    float k_scale, float v_scale, int dv) {
   using RC = RopeChunk<__bf16, D, HALF>;
   constexpr int U = RC::U, NP = RC::NP;  // units of 8 elements
   const int64_t gid = (int64_t)blockIdx.x * kRopeThreads + threadIdx.x;
@@ -384,15 +385,16 @@ __global__ __launch_bounds__(kRopeThreads) void rope_fp8_kernel(
   };
   rows(q, qs, q_scale, qo, H);
   rows(k, ks, k_scale, ko, Hk);
+  const int UV = dv / 8;  // V rows: dv codes, UV units of 8 over the token's U/2 lanes
   const uint2 *v8 = reinterpret_cast<const uint2 *>(v + n * vs);
-  uint4 *v4 = reinterpret_cast<uint4 *>(vo + n * (int64_t)Hk * D);
+  uint4 *v4 = reinterpret_cast<uint4 *>(vo + n * (int64_t)Hk * dv);
   for (int hh = 0; hh < Hk; ++hh) {
-    float a[8], b[8];
-    unpack_fp8(v8[hh * U + c], v_scale, a);
-    unpack_fp8(v8[hh * U + c + U / 2], v_scale, b);
-    const int ob = out_head(hh) * U;
-    v4[ob + c] = pack<__bf16>(a);
-    v4[ob + c + U / 2] = pack<__bf16>(b);
+    const int ob = out_head(hh) * UV;
+    for (int u = c; u < UV; u += U / 2) {
+      float a[8];
+      unpack_fp8(v8[hh * UV + u], v_scale, a);
+      v4[ob + u] = pack<__bf16>(a);
+    }
   }
 }
 
@@ -416,7 +418,7 @@ hipError_t launch_fp8_typed(const attn_plan *p, const void *q, int64_t qs, const
 #define F8_LAUNCH(HF, PMV, NRM)                                                                 \
   hipLaunchKernelGGL((rope_fp8_kernel<D, HF, PMV, NRM>), grid, dim3(kRopeThreads), 0, stream, Q, \
                      qs, K, ks, Vv, vs, QO, KO, VO, pos, tc, ts, N, p->p.H, p->p.Hkv, eps,       \
-                     scales[0], scales[1], scales[2])
+                     scales[0], scales[1], scales[2], p->p.dv)
 #define F8_PM(HF, NRM)                         \
   do {                                         \
     if (pm == 0) F8_LAUNCH(HF, 0, NRM);        \
@@ -466,7 +468,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_bwd_kernel(
     const T *__restrict__ q, int64_t qs, const T *__restrict__ k, int64_t ks, const float *dq_in,
     const float *dk_in, const float *dv_in, float *dq, float *dk, float *dv,
     const int32_t *__restrict__ tok_pos, const float *__restrict__ tcos,
-    const float *__restrict__ tsin, int64_t N, int H, int Hk, float eps) {
+    const float *__restrict__ tsin, int64_t N, int H, int Hk, float eps, int dv_dim) {
   using RC = RopeChunk<float, D, HALF>;  // fp32 units of 4
   constexpr int U = RC::U, NP = RC::NP, L = U / 2;
   const int64_t gid = (int64_t)blockIdx.x * kRopeThreads + threadIdx.x;
@@ -525,13 +527,13 @@ __global__ __launch_bounds__(kRopeThreads) void rope_bwd_kernel(
   };
   rows(dq_in, dq, q, qs, H);
   rows(dk_in, dk, k, ks, Hk);
-  if (dv) {
-    const uint4 *v4 = reinterpret_cast<const uint4 *>(dv_in + n * (int64_t)Hk * D);
-    uint4 *o4 = reinterpret_cast<uint4 *>(dv + n * (int64_t)Hk * D);
+  if (dv) {  // dV rows: dv_dim floats, UV units of 4 over the token's L lanes
+    const int UV = dv_dim / 4;
+    const uint4 *v4 = reinterpret_cast<const uint4 *>(dv_in + n * (int64_t)Hk * dv_dim);
+    uint4 *o4 = reinterpret_cast<uint4 *>(dv + n * (int64_t)Hk * dv_dim);
     for (int hh = 0; hh < Hk; ++hh) {
-      const int sb = slot_head(hh) * U;
-      o4[hh * U + c] = v4[sb + c];
-      o4[hh * U + c + U / 2] = v4[sb + c + U / 2];
+      const int sb = slot_head(hh) * UV;
+      for (int u = c; u < UV; u += L) o4[hh * UV + u] = v4[sb + u];
     }
   }
 }
@@ -554,7 +556,7 @@ hipError_t launch_bwd_typed(const attn_plan *p, const void *q, int64_t qs, const
 #define RB_LAUNCH(HF, PMV, NRM)                                                                 \
   hipLaunchKernelGGL((rope_bwd_kernel<T, D, HF, PMV, NRM>), grid, dim3(kRopeThreads), 0, stream, \
                      Q, qs, K, ks, dqi, dki, dvi, dq, dk, dv, pos, tc, ts, N, p->p.H, p->p.Hkv,  \
-                     eps)
+                     eps, p->p.dv)
 #define RB_PM(HF, NRM)                         \
   do {                                         \
     if (pm == 0) RB_LAUNCH(HF, 0, NRM);        \

@@ -39,6 +39,7 @@ class Workload:
     rope: int
     paired: int = 0
     kv_heads: int = 0             # K/V heads (grouped-query); 0 -> heads
+    v_dim: int = 0                # width of V, O, dO rows; 0 -> head_dim
     causal: int = 1
     window: int = 0               # key slots, self included; <= 0: none
     scale: float = 0.0            # 0 -> 1/sqrt(head_dim)
@@ -94,18 +95,19 @@ def cu_seqlens(w: Workload, seed: Optional[int] = None) -> np.ndarray:
 
 
 def tensors(w: Workload, seed: Optional[int] = None, with_grad: Optional[bool] = None):
-    """Q, K, V (and dO) as CPU tensors [N, H, d] (K, V: [N, Hkv, d] when grouped)
-    in the workload's dtype."""
+    """Q, K, V (and dO) as CPU tensors [N, H, d] (K, V: [N, Hkv, d] when grouped;
+    V and dO rows have v_dim elements when it is set) in the workload's dtype."""
     seed = w.num if seed is None else seed
     with_grad = w.backward if with_grad is None else with_grad
     g = torch.Generator().manual_seed(seed)
-    shape = (w.n_tokens, w.heads, w.head_dim)
-    kv_shape = (w.n_tokens, w.kv_heads or w.heads, w.head_dim)
+    dv = w.v_dim or w.head_dim
+    hk = w.kv_heads or w.heads
+    shapes = {"q": (w.n_tokens, w.heads, w.head_dim), "k": (w.n_tokens, hk, w.head_dim),
+              "v": (w.n_tokens, hk, dv), "do": (w.n_tokens, w.heads, dv)}
     names = ["q", "k", "v"] + (["do"] if with_grad else [])
     out = {}
     for n in names:
-        out[n] = torch.randn(kv_shape if n in ("k", "v") else shape, generator=g,
-                             dtype=torch.float32).to(w.torch_dtype)
+        out[n] = torch.randn(shapes[n], generator=g, dtype=torch.float32).to(w.torch_dtype)
     return out
 
 
@@ -121,11 +123,12 @@ def fp8_tensors(w: Workload, seed: Optional[int] = None):
     per-tensor float32 scales (q, k, v)."""
     seed = w.num if seed is None else seed
     g = torch.Generator().manual_seed(seed)
-    shape = (w.n_tokens, w.heads, w.head_dim)
-    kv_shape = (w.n_tokens, w.kv_heads or w.heads, w.head_dim)
+    hk = w.kv_heads or w.heads
+    shapes = {"q": (w.n_tokens, w.heads, w.head_dim), "k": (w.n_tokens, hk, w.head_dim),
+              "v": (w.n_tokens, hk, w.v_dim or w.head_dim)}
     out, scales = {}, []
     for n in ("q", "k", "v"):
-        x = torch.randn(kv_shape if n in ("k", "v") else shape, generator=g, dtype=torch.float32)
+        x = torch.randn(shapes[n], generator=g, dtype=torch.float32)
         amax = float(x.abs().max()) if x.numel() else 1.0
         sc = float(np.float32(max(amax, 1e-30) / 448.0))
         out[n] = (x / sc).to(torch.float8_e4m3fn).view(torch.uint8)
