@@ -108,19 +108,23 @@ def test_item_sizes_follow_the_dtype():
     # bf16: 256-query forward items, 128-row backward dK/dV (keys) and dQ
     # (queries) items; fp32 (no backward): 128-query forward items and empty
     # backward lists
-    cu = [0, 700]
-    pb = plan(num_tokens=700, cu_seqlens=cu)
-    pb128 = plan(num_tokens=700, cu_seqlens=cu, head_dim=128)
-    pf = plan(num_tokens=700, cu_seqlens=cu, dtype="fp32")
+    cu = [0, 2100]
+    pb = plan(num_tokens=2100, cu_seqlens=cu)
+    pb128 = plan(num_tokens=2100, cu_seqlens=cu, head_dim=128)
+    pf = plan(num_tokens=2100, cu_seqlens=cu, dtype="fp32")
     rows = lambda p, which: np.diff(p.work_items(which)[:, 1:3], axis=1).max()
     assert rows(pb, 0) == 256 and rows(pb, 1) == 128 and rows(pb, 2) == 128
     assert rows(pb128, 0) == 256 and rows(pb128, 1) == 128 and rows(pb128, 2) == 128
     assert rows(pf, 0) == 128
     # a short window keeps 128-query forward items (a longer one does not)
-    assert np.diff(plan(num_tokens=700, cu_seqlens=cu, window=512).work_items(0)[:, 1:3],
+    assert np.diff(plan(num_tokens=2100, cu_seqlens=cu, window=512).work_items(0)[:, 1:3],
                    axis=1).max() == 128
-    assert np.diff(plan(num_tokens=700, cu_seqlens=cu, window=513).work_items(0)[:, 1:3],
+    assert np.diff(plan(num_tokens=2100, cu_seqlens=cu, window=513).work_items(0)[:, 1:3],
                    axis=1).max() == 256
+    # so do problems whose sequences all have at most 2048 slots (paired: 1024 tokens)
+    assert rows(plan(num_tokens=2048, cu_seqlens=[0, 2048]), 0) == 128
+    assert rows(plan(num_tokens=2049, cu_seqlens=[0, 2049]), 0) == 256
+    assert rows(plan(num_tokens=1025, cu_seqlens=[0, 1025], paired=1), 0) == 256
     assert len(pf.work_items(1)) == 0 and len(pf.work_items(2)) == 0
     for bad in (-1, 3):
         with pytest.raises(tca.AttnError):
@@ -186,7 +190,7 @@ def test_counts_and_work_lists_cover_the_mask(cu, H, paired, causal, window):
     fwd = p.work_items(0)
     bwd = p.work_items(1)
     dq = p.work_items(2)
-    # forward (256-query items for bf16) and dQ (128-query items): every
+    # forward (128- or 256-query items for bf16) and dQ (128-query items): every
     # (head, query) row exactly once; its visible keys inside [k0, k1)
     bounds = np.array(cu) * mult
     def seq_of(slot):

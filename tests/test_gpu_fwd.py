@@ -176,9 +176,12 @@ EDGE = [
     ("fp32 varlen window", 3, 128, wl.DTYPE_FP32, [0, 70, 200, 333], 0, 100, 2),
     ("fp32 paired", 4, 64, wl.DTYPE_FP32, [0, 129, 200], 1, 0, 1),
     ("single token", 2, 64, wl.DTYPE_BF16, [0, 1], 0, 0, 1),
-    # windows past 512 slots run the 256-query items of the bf16 kernel
-    ("window 513", 2, 64, wl.DTYPE_BF16, [0, 1100], 0, 513, 1),
-    ("paired H2 window 600", 2, 128, wl.DTYPE_BF16, [0, 300, 1000], 1, 600, 2),
+    # windows past 512 slots over sequences past 2048 slots run the 256-query
+    # items of the bf16 kernel (shorter ones run 128-query items)
+    ("window 513", 2, 64, wl.DTYPE_BF16, [0, 2200], 0, 513, 1),
+    ("paired H2 window 600", 2, 128, wl.DTYPE_BF16, [0, 300, 1400], 1, 600, 2),
+    ("causal 2300 slots d64", 2, 64, wl.DTYPE_BF16, [0, 150, 2450], 0, 0, 1),
+    ("causal 2049 slots d128", 2, 128, wl.DTYPE_BF16, [0, 2049], 0, 0, 2),
 ]
 
 

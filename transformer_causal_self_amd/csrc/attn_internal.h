@@ -15,11 +15,13 @@ namespace attn {
 //   forward: BQ query slots per work item, BK key slots per inner step, 32
 //   queries per wave.  bf16 runs eight waves per item (each staged K/V tile
 //   serves 256 queries) unless the window is short, where a 256-query item
-//   would stage mostly keys that most of its waves skip: then four.  fp32 runs
-//   four, its registers do not allow more.
+//   would stage mostly keys that most of its waves skip, or every sequence is
+//   short, where twice as many items balance the CUs better: then four.  fp32
+//   runs four, its registers do not allow more.
 constexpr int kFwdBQ = 256;
 constexpr int kFwdBQShort = 128;
 constexpr int kFwdShortWindow = 512;  // windows up to this use kFwdBQShort
+constexpr int kFwdShortSeq = 2048;    // and so do problems whose sequences all fit this
 constexpr int kFwdBQF32 = 128;
 constexpr int kFwdThreadsF32 = 256;
 constexpr int kFwdBK = 64;

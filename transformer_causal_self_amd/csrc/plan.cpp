@@ -233,9 +233,9 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
     int64_t pairs = 0;
     int stream = 0;
     const bool bf16 = P.dtype == ATTN_BF16;  // the backward is bf16 only
-    p->fwd_bq = !bf16 ? attn::kFwdBQF32
-                : (P.window > 0 && P.window <= attn::kFwdShortWindow) ? attn::kFwdBQShort
-                                                                      : attn::kFwdBQ;
+    const bool short_rows = (P.window > 0 && P.window <= attn::kFwdShortWindow) ||
+                            max_len * mult <= attn::kFwdShortSeq;
+    p->fwd_bq = !bf16 ? attn::kFwdBQF32 : short_rows ? attn::kFwdBQShort : attn::kFwdBQ;
     // One stream per (K/V head, sequence).  With grouped K/V heads, the items
     // of the group's query heads are interleaved tile by tile, so the ones
     // that read the same K/V rows land in one chunk (one XCD, one L2).
