@@ -132,7 +132,8 @@ typedef struct {
   int64_t bwd_items;         /* key-tile work items of the backward */
   int64_t slots;             /* N' */
   int32_t attn_heads;        /* H' */
-  int32_t max_positions;     /* rows of the rotary table */
+  int32_t max_positions;     /* positions the rotary table covers (longest
+                                sequence, doubled when paired) */
   int32_t kv_heads;          /* K/V heads: Hkv, or H' when not grouped */
   int32_t v_head_dim;        /* dv */
 } attn_plan_info;
@@ -140,8 +141,11 @@ typedef struct {
 /*
  * Validate a problem and build its host plan: paired slot boundaries
  * (2 * cu when paired), the per-token rotary positions, the fp64-computed
- * cos/sin table rounded to fp32, and the tile work lists (fully masked causal
- * and window tiles are never listed; longest items first).  Host only: makes
+ * cos/sin table rounded to fp32 (two levels: angles lo * theta and
+ * 64 hi * theta, combined by angle addition in the kernels for position
+ * 64 hi + lo, so the table stays cache resident), and the tile work lists
+ * (fully masked causal and window tiles are never listed; longest items
+ * first).  Host only: makes
  * no HIP call.  On success *out owns a plan to free with attn_plan_destroy.
  * Errors: ATTN_E_INVALID (bad field), ATTN_E_UNSUPPORTED (head_dim or
  * v_head_dim not 64 or 128; v_head_dim != head_dim with fp32; grouped K/V

@@ -32,8 +32,10 @@ constexpr int kFwdBK = 64;
 constexpr int kBwdWaves = 4;
 constexpr int kBwdRows = 32 * kBwdWaves;
 constexpr int kBwdBQ = 64;
-//   rotary: threads per block.
+//   rotary: threads per block, and the fine step of the two-level cos/sin
+//   table (positions p = hi * kRopeFine + lo).
 constexpr int kRopeThreads = 256;
+constexpr int kRopeFine = 64;
 // Work-list chunk: consecutive tiles of one head and sequence kept on one XCD.
 constexpr int kXcdChunk = 16;
 
@@ -74,9 +76,9 @@ struct attn_plan {
   attn::Problem p;
   std::vector<int32_t> cu;          // token boundaries, S + 1
   std::vector<int32_t> tok_pos;     // per token: offset inside its sequence
-  std::vector<float> rope_cos;      // [P, d/2]
-  std::vector<float> rope_sin;      // [P, d/2]
-  int32_t max_pos = 0;              // P
+  std::vector<float> rope_cos;      // [F + ceil(P / F), d/2]: fine rows, then coarse
+  std::vector<float> rope_sin;      // same layout (F = kRopeFine)
+  int32_t max_pos = 0;              // P, positions covered
   int32_t fwd_bq = 0;               // query slots per forward item
   std::vector<attn::WorkItem> fwd;  // forward items
   std::vector<attn::WorkItem> bwd;  // dK/dV items

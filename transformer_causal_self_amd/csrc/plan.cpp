@@ -211,22 +211,29 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
     for (int s = 0; s < S; ++s)
       for (int32_t n = cu[s]; n < cu[s + 1]; ++n) p->tok_pos[(size_t)n] = n - cu[s];
 
-    // Rotary table: cos and sin of p * base^(-2i/d), computed in fp64 and
-    // rounded once to fp32 ("Upgrading a textbook decoder", section 2).  Paired
-    // positions reach 2t + 1, so the table doubles.
+    // Rotary table: cos and sin of angles p * base^(-2i/d) ("Upgrading a
+    // textbook decoder", section 2), computed in fp64 and rounded once to
+    // fp32.  Paired positions reach 2t + 1, so the range doubles.  Two levels,
+    // so that the table stays in every XCD's L2: rows [0, F) hold the angles
+    // lo * theta_i, rows F + hi the angles hi * F * theta_i (F = kRopeFine); the
+    // kernels form position p = hi * F + lo by the angle-addition formulas.
     if (P.rope != ATTN_ROPE_NONE) {
       const int half = P.d / 2;
+      constexpr int F = attn::kRopeFine;
       p->max_pos = (int32_t)std::max<int64_t>(1, max_len * mult);
-      p->rope_cos.resize((size_t)p->max_pos * half);
-      p->rope_sin.resize((size_t)p->max_pos * half);
+      const int32_t rows = F + (p->max_pos + F - 1) / F;
+      p->rope_cos.resize((size_t)rows * half);
+      p->rope_sin.resize((size_t)rows * half);
       std::vector<double> theta(half);
       for (int i = 0; i < half; ++i) theta[i] = std::pow(P.rope_base, -2.0 * i / (double)P.d);
-      for (int32_t pos = 0; pos < p->max_pos; ++pos)
+      for (int32_t r = 0; r < rows; ++r) {
+        const double step = r < F ? (double)r : (double)(r - F) * F;
         for (int i = 0; i < half; ++i) {
-          const double phi = (double)pos * theta[i];
-          p->rope_cos[(size_t)pos * half + i] = (float)std::cos(phi);
-          p->rope_sin[(size_t)pos * half + i] = (float)std::sin(phi);
+          const double phi = step * theta[i];
+          p->rope_cos[(size_t)r * half + i] = (float)std::cos(phi);
+          p->rope_sin[(size_t)r * half + i] = (float)std::sin(phi);
         }
+      }
     }
 
     // Work lists and exact counts.

@@ -86,6 +86,20 @@ __device__ __forceinline__ float lanes_sum(float v) {
   return v;
 }
 
+// cos and sin of angle column `col` at position `pos` from the two-level
+// table: rows [0, F) hold lo * theta, rows F + hi hold hi * F * theta
+// (F = kRopeFine); pos = hi * F + lo by the angle-addition formulas.
+template <int D>
+__device__ __forceinline__ void table_angle(const float *__restrict__ tcos,
+                                            const float *__restrict__ tsin, int64_t pos, int col,
+                                            float &c, float &s) {
+  const int64_t lo = pos & (kRopeFine - 1), hi = kRopeFine + pos / kRopeFine;
+  const float c1 = tcos[lo * (D / 2) + col], s1 = tsin[lo * (D / 2) + col];
+  const float c2 = tcos[hi * (D / 2) + col], s2 = tsin[hi * (D / 2) + col];
+  c = fmaf(c2, c1, -s2 * s1);
+  s = fmaf(s2, c1, c2 * s1);
+}
+
 // Work split: a row of D elements is U = D / V sixteen-byte units (V elements
 // each).  Thread (token n, chunk c) owns units c and c + U/2 of every head row of
 // that token, so each load/store instruction of a wave covers whole 128-byte
@@ -174,12 +188,9 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
 #pragma unroll
   for (int par = 0; par < (PM ? 2 : 1); ++par) {
     const int64_t pos = PM ? 2 * t + par : t;
-    const float *cr = tcos + pos * (D / 2), *sr = tsin + pos * (D / 2);
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      cs[par][i] = cr[RC::col(c, i)];
-      sn[par][i] = sr[RC::col(c, i)];
-    }
+    for (int i = 0; i < NP; ++i)
+      table_angle<D>(tcos, tsin, pos, RC::col(c, i), cs[par][i], sn[par][i]);
   }
   const uint4 *q4 = reinterpret_cast<const uint4 *>(q + n * qs);
   const uint4 *k4 = reinterpret_cast<const uint4 *>(k + n * ks);
@@ -353,12 +364,9 @@ __global__ __launch_bounds__(kRopeThreads) void rope_fp8_kernel(
 #pragma unroll
   for (int par = 0; par < (PM ? 2 : 1); ++par) {
     const int64_t pos = PM ? 2 * t + par : t;
-    const float *cr = tcos + pos * (D / 2), *sr = tsin + pos * (D / 2);
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      cs[par][i] = cr[RC::col(c, i)];
-      sn[par][i] = sr[RC::col(c, i)];
-    }
+    for (int i = 0; i < NP; ++i)
+      table_angle<D>(tcos, tsin, pos, RC::col(c, i), cs[par][i], sn[par][i]);
   }
   auto out_head = [H](int hh) { return PM == 2 ? (hh & 1) * (H / 2) + hh / 2 : hh; };
   auto rows = [&](const uint8_t *src, int64_t ss, float scale, __bf16 *dst, int nh) {
@@ -480,11 +488,10 @@ __global__ __launch_bounds__(kRopeThreads) void rope_bwd_kernel(
 #pragma unroll
   for (int par = 0; par < (PM ? 2 : 1); ++par) {
     const int64_t pos = PM ? 2 * t + par : t;
-    const float *cr = tcos + pos * (D / 2), *sr = tsin + pos * (D / 2);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      cs[par][i] = cr[RC::col(c, i)];
-      sn[par][i] = -sr[RC::col(c, i)];
+      table_angle<D>(tcos, tsin, pos, RC::col(c, i), cs[par][i], sn[par][i]);
+      sn[par][i] = -sn[par][i];
     }
   }
   auto slot_head = [H](int hh) { return PM == 2 ? (hh & 1) * (H / 2) + hh / 2 : hh; };
