@@ -12,17 +12,19 @@
 // rowsum(dP o P) = D_i, not the variant printed in the "mHC module" article
 // (lshu.cn, section 4.1), which is not the derivative of softmax.
 //
-// Three kernels, deterministic (no atomics):
+// Two launches, deterministic without grouped K/V heads (no atomics):
 //   1. delta:  D_i for every (attention head, slot).
-//   2. dK/dV:  one block per 128-key tile of one attention head (32 keys per
+//   2. one grid of two item kinds (the dQ items fill the CUs that the dK/dV
+//      tail leaves idle):
+//      dK/dV:  one block per 128-key tile of one attention head (32 keys per
 //              wave), looping over the 64-query tiles that can see it.  S is
 //              formed as Q K^T so that every accumulator lane belongs to one
 //              key; P^T and dS^T then feed the MFMA A operand straight from
 //              registers, and Q^T / dO^T are staged transposed in LDS with the
 //              matching row permutation.
-//   3. dQ:     one block per 128-query tile (the forward's work list), looping
-//              over key tiles; S^T = K Q^T as in the forward, K^T staged
-//              transposed for dQ^T = K^T dS^T.
+//      dQ:     one block per 128-query tile, looping over key tiles;
+//              S^T = K Q^T as in the forward, K^T staged transposed for
+//              dQ^T = K^T dS^T.
 #include "attn_internal.h"
 #include "device_common.h"
 #include "launch.h"
@@ -144,16 +146,16 @@ struct DkvSmem {
   DkvBuf<D, DV> b[2];  // double buffered: one barrier per query tile
 };
 
+// One dK/dV item (keys [q0, q1), queries [k0, k1)).
 template <int D, int DV, int NW>
-__global__ __launch_bounds__(64 * NW, (bwd_min_blocks<D, DV>())) void dkv_kernel(
-    const WorkItem *__restrict__ items, const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
-    const __bf16 *__restrict__ V, const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
-    const float *__restrict__ delta, float *__restrict__ dK, float *__restrict__ dV, int Hs,
-    int Hks, int G, int64_t Ns, float scale, float scale_log2, int causal, int window) {
+__device__ __forceinline__ void dkv_item(
+    const WorkItem it, DkvSmem<D, DV> &sm, const __bf16 *__restrict__ Q,
+    const __bf16 *__restrict__ K, const __bf16 *__restrict__ V, const __bf16 *__restrict__ dO,
+    const float *__restrict__ LSE, const float *__restrict__ delta, float *__restrict__ dK,
+    float *__restrict__ dV, int Hs, int Hks, int G, int64_t Ns, float scale, float scale_log2,
+    int causal, int window) {
   constexpr int RS = DkvBuf<D, DV>::RS, RSV = DkvBuf<D, DV>::RSV, TS = DkvBuf<D, DV>::TS;
   constexpr int BQ = kBwdBQ;
-  __shared__ __attribute__((aligned(16))) DkvSmem<D, DV> sm;
-  const WorkItem it = items[blockIdx.x];  // keys [q0, q1), queries [k0, k1)
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int h = lane >> 5, l32 = lane & 31;
@@ -322,17 +324,15 @@ struct DqSmem {
   DqBuf<D, DV> b[2];  // double buffered: one barrier per key tile
 };
 
+// One dQ item (queries [q0, q1), keys [k0, k1)).
 template <int D, int DV, int NW>
-__global__ __launch_bounds__(64 * NW, (bwd_min_blocks<D, DV>())) void dq_kernel(
-    const WorkItem *__restrict__ items, const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
-    const __bf16 *__restrict__ V, const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
-    const float *__restrict__ delta, float *__restrict__ dQ, int Hs, int Hks, int G, int64_t Ns,
-    float scale,
-    float scale_log2, int causal, int window) {
+__device__ __forceinline__ void dq_item(
+    const WorkItem it, DqSmem<D, DV> &sm, const __bf16 *__restrict__ Q,
+    const __bf16 *__restrict__ K, const __bf16 *__restrict__ V, const __bf16 *__restrict__ dO,
+    const float *__restrict__ LSE, const float *__restrict__ delta, float *__restrict__ dQ,
+    int Hs, int Hks, int G, int64_t Ns, float scale, float scale_log2, int causal, int window) {
   constexpr int RS = DqBuf<D, DV>::RS, RSV = DqBuf<D, DV>::RSV, TS = DqBuf<D, DV>::TS;
   constexpr int BK = kFwdBK;
-  __shared__ __attribute__((aligned(16))) DqSmem<D, DV> sm;
-  const WorkItem it = items[blockIdx.x];  // queries [q0, q1), keys [k0, k1)
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int h = lane >> 5, l32 = lane & 31;
@@ -461,6 +461,29 @@ __global__ __launch_bounds__(64 * NW, (bwd_min_blocks<D, DV>())) void dq_kernel(
   }
 }
 
+// Both passes in one launch: blocks [0, n_dkv) run the dK/dV items, the rest
+// the dQ items, so the dQ work fills the CUs the dK/dV tail leaves idle.  The
+// two share one LDS allocation (the larger of the two layouts).
+template <int D, int DV, int NW>
+__global__ __launch_bounds__(64 * NW, (bwd_min_blocks<D, DV>())) void bwd_kernel(
+    const WorkItem *__restrict__ dkv_items, int n_dkv, const WorkItem *__restrict__ dq_items,
+    const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
+    const __bf16 *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ delta,
+    float *__restrict__ dQ, float *__restrict__ dK, float *__restrict__ dV, int Hs, int Hks, int G,
+    int64_t Ns, float scale, float scale_log2, int causal, int window) {
+  __shared__ __attribute__((aligned(16))) union {
+    DkvSmem<D, DV> kv;
+    DqSmem<D, DV> q;
+  } sm;
+  const int b = (int)blockIdx.x;
+  if (b < n_dkv)
+    dkv_item<D, DV, NW>(dkv_items[b], sm.kv, Q, K, V, dO, LSE, delta, dK, dV, Hs, Hks, G, Ns,
+                        scale, scale_log2, causal, window);
+  else
+    dq_item<D, DV, NW>(dq_items[b - n_dkv], sm.q, Q, K, V, dO, LSE, delta, dQ, Hs, Hks, G, Ns,
+                       scale, scale_log2, causal, window);
+}
+
 // Zero na floats of a and nb of b (dK and dV before the grouped heads add
 // into them; a kernel rather than a memset, so the launch sequence stays
 // graph-capturable).
@@ -492,15 +515,13 @@ hipError_t launch_typed(const attn_plan *p, const void *q, const void *k, const 
     hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, dk,
                        nk, dv, nv);
   }
-  if (!p->bwd.empty())
-    hipLaunchKernelGGL((dkv_kernel<D, DV, NWK>), dim3((unsigned)p->bwd.size()), dim3(64 * NWK), 0,
-                       stream, reinterpret_cast<const WorkItem *>(p->ws + p->off_bwd), Q, K, V, G,
-                       lse, delta, dk, dv, Hs, p->p.Hks, p->p.G, Ns, scale, scale_log2,
-                       p->p.causal, p->p.window);
-  if (!p->dq.empty())
-    hipLaunchKernelGGL((dq_kernel<D, DV, NWQ>), dim3((unsigned)p->dq.size()), dim3(64 * NWQ), 0,
-                       stream, reinterpret_cast<const WorkItem *>(p->ws + p->off_dq), Q, K, V, G,
-                       lse, delta, dq, Hs, p->p.Hks, p->p.G, Ns, scale, scale_log2,
+  static_assert(NWK == NWQ, "one launch runs both passes");
+  const unsigned nb = (unsigned)(p->bwd.size() + p->dq.size());
+  if (nb > 0)
+    hipLaunchKernelGGL((bwd_kernel<D, DV, NWK>), dim3(nb), dim3(64 * NWK), 0, stream,
+                       reinterpret_cast<const WorkItem *>(p->ws + p->off_bwd), (int)p->bwd.size(),
+                       reinterpret_cast<const WorkItem *>(p->ws + p->off_dq), Q, K, V, G, lse,
+                       delta, dq, dk, dv, Hs, p->p.Hks, p->p.G, Ns, scale, scale_log2,
                        p->p.causal, p->p.window);
   return hipGetLastError();
 }
