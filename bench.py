@@ -66,6 +66,8 @@ def kernel_sources_digest():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "transformer_causal_self_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if not name.endswith((".hip", ".h", ".cpp")):
+            continue            # build by-products are not sources
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]

@@ -165,3 +165,17 @@ def test_fp8_rejects():
     fp32 = tca.attn_plan_create(64, 2, 64, "fp32", cu).bind("cuda")
     assert call(c, 128, sc(1, 1, 1), fp32) == UNSUPPORTED
     torch.cuda.synchronize()
+
+
+def test_fp8_full_size():
+    """Problem 4's full size (65536 tokens, H = 6, d = 128, ragged documents)
+    with FP8 inputs, in the launch configuration the benchmark times."""
+    w = W[4]
+    inp = wl.fp8_tensors(w)
+    say(f"fp8 rope full size N={w.n_tokens}")
+    plan = plan_of(w, inp["cu"])
+    q2, k2, v2 = run(w, inp, plan)
+    qr, kr, _ = prepared(w, inp, False)
+    assert_close(q2.cpu().double().numpy(), qr, tol(w), "q'")
+    assert_close(k2.cpu().double().numpy(), kr, tol(w), "k'")
+    assert torch.equal(v2.cpu(), v_expected(inp["v"], inp["scales"][2]))
