@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=30.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--paired", type=int, choices=(0, 1, 2), default=None,
                     help="override the workload's head pairing (2: adjacent partner h^1, "
