@@ -264,23 +264,37 @@ __global__ __launch_bounds__(kFwdThreadsF32, fwd_min_blocks<T>()) void fwd_kerne
 // tile max exceeds it by more than 2^8 in the exp2 domain (the weights stay
 // below 256, so nothing overflows, and O / l is unchanged).
 
-// D: width of Q and K rows; DV: width of V and O rows.
-template <int D, int DV>
+// D: width of Q and K rows; DV: width of V and O rows.  K is kept row-major
+// (one key per row).  V has two layouts (VT):
+//   VT = true:  V^T, the key order permuted to the order the S accumulator
+//               holds (perm16), so one 16-byte read gives the PV A operand;
+//               staging it costs eight 4-byte stores and byte permutes per
+//               16 bytes.
+//   VT = false: row-major like K (one 16-byte store), read transposed with
+//               two ds_read_b64_tr_b16, which run at half the rate of
+//               16-byte reads.
+// Eight-wave items read every staged tile eight times and use VT = true;
+// four-wave items (short windows, short sequences) use VT = false, where the
+// cheaper store wins (10% on the paired window-128 problem; the other way
+// round costs 3-7% on eight-wave items).
+template <int D, int DV, bool VT>
 struct SmemBF {
-  static constexpr int KS = D + 8;   // K row stride (elements): 16-byte rows, 4-bank shift
-  static constexpr int VS = BK + 8;  // V^T row stride (elements)
+  static constexpr int KS = D + 8;                 // K row stride (elements): 4-bank shift
+  static constexpr int VS = VT ? BK + 8 : DV + 8;  // V^T or V row stride (elements)
   __bf16 k[2][BK * KS];
-  __bf16 vt[2][DV * VS];
+  __bf16 v[2][VT ? DV * VS : BK * VS];
 };
 
-template <int D, int DV, int NT>
+template <int D, int DV, int NT, bool VT>
 struct StageBF {
   static constexpr int KPT = BK * D / 8 / NT;  // 16-byte K chunks per thread
   static_assert(KPT >= 1 && BK * D / 8 % NT == 0, "K staging split");
-  static constexpr int VU = (BK / 2) * (DV / 8);  // (key pair, 8 features) units per tile
+  // V units: (key pair, 8 features) for VT, else 16-byte chunks of one key
+  static constexpr int VR = VT ? 2 : 1;  // rows per unit
+  static constexpr int VU = (BK / VR) * (DV / 8);
   static constexpr int VPT = (VU + NT - 1) / NT;
   uint4 kr[KPT];
-  uint4 vr[VPT][2];
+  uint4 vr[VPT][VR];
 
   // Rows [kt0, kt0 + BK) of the head's K and V (row strides rsb, rsbv bytes);
   // rows past `rows` read zero.
@@ -298,14 +312,18 @@ struct StageBF {
     for (int r = 0; r < VPT; ++r) {
       const int vi = tid + NT * r;
       if (VU % NT != 0 && vi >= VU) break;
-      const uint32_t off = (uint32_t)(2 * (vi % (BK / 2))) * rsbv + 16u * (vi / (BK / 2));
-      vr[r][0] = buf_load16(rv, off);
-      vr[r][1] = buf_load16(rv, off + rsbv);
+      if (VT) {
+        const uint32_t off = (uint32_t)(2 * (vi % (BK / 2))) * rsbv + 16u * (vi / (BK / 2));
+        vr[r][0] = buf_load16(rv, off);
+        vr[r][VR - 1] = buf_load16(rv, off + rsbv);
+      } else {
+        vr[r][0] = buf_load16(rv, (uint32_t)(vi / (DV / 8)) * rsbv + 16u * (vi % (DV / 8)));
+      }
     }
   }
 
-  __device__ __forceinline__ void store(__bf16 *kdst, __bf16 *vtdst, int tid) const {
-    constexpr int KS = SmemBF<D, DV>::KS, VS = SmemBF<D, DV>::VS;
+  __device__ __forceinline__ void store(__bf16 *kdst, __bf16 *vdst, int tid) const {
+    constexpr int KS = SmemBF<D, DV, VT>::KS, VS = SmemBF<D, DV, VT>::VS;
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int ci = tid + NT * r;
@@ -315,15 +333,20 @@ struct StageBF {
     for (int r = 0; r < VPT; ++r) {
       const int vi = tid + NT * r;
       if (VU % NT != 0 && vi >= VU) break;
-      const int kp = vi % (BK / 2), c8 = vi / (BK / 2);
-      const int pos = perm16(2 * kp);  // even; key 2kp+1 lands at pos + 1
-      const uint32_t a[4] = {vr[r][0].x, vr[r][0].y, vr[r][0].z, vr[r][0].w};
-      const uint32_t b[4] = {vr[r][1].x, vr[r][1].y, vr[r][1].z, vr[r][1].w};
+      if (VT) {
+        const int kp = vi % (BK / 2), c8 = vi / (BK / 2);
+        const int pos = perm16(2 * kp);  // even; key 2kp+1 lands at pos + 1
+        const uint4 &ra = vr[r][0], &rb = vr[r][VR - 1];
+        const uint32_t a[4] = {ra.x, ra.y, ra.z, ra.w};
+        const uint32_t b[4] = {rb.x, rb.y, rb.z, rb.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t word = (e & 1) ? __byte_perm(a[e / 2], b[e / 2], 0x7632)
-                                      : __byte_perm(a[e / 2], b[e / 2], 0x5410);
-        *reinterpret_cast<uint32_t *>(&vtdst[(8 * c8 + e) * VS + pos]) = word;
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t word = (e & 1) ? __byte_perm(a[e / 2], b[e / 2], 0x7632)
+                                        : __byte_perm(a[e / 2], b[e / 2], 0x5410);
+          *reinterpret_cast<uint32_t *>(&vdst[(8 * c8 + e) * VS + pos]) = word;
+        }
+      } else {
+        *reinterpret_cast<uint4 *>(&vdst[(vi / (DV / 8)) * VS + 8 * (vi % (DV / 8))]) = vr[r][0];
       }
     }
   }
@@ -369,8 +392,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
     const WorkItem *__restrict__ items, const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const __bf16 *__restrict__ V, __bf16 *__restrict__ O, float *__restrict__ LSE, int Hs,
     int Hks, int G, int64_t Ns, float scale, float scale_log2, int causal, int window) {
-  constexpr int KS = SmemBF<D, DV>::KS, VS = SmemBF<D, DV>::VS;
-  __shared__ __attribute__((aligned(16))) SmemBF<D, DV> sm;
+  constexpr bool VT = NW == 8;  // V layout (see SmemBF)
+  constexpr int KS = SmemBF<D, DV, VT>::KS, VS = SmemBF<D, DV, VT>::VS;
+  __shared__ __attribute__((aligned(16))) SmemBF<D, DV, VT> sm;
   const WorkItem it = items[blockIdx.x];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -387,6 +411,12 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
   const int wq1 = min(wq0 + 32, it.q1);  // one past its last valid query
   const int qi = wq0 + l32;              // this lane's query
   const bool qok = qi < it.q1;
+  // this lane's part of a V read: VT, row l32 of V^T at key column 8h;
+  // else a transposed read, where inside its group of 16 lanes, lane 4e + g
+  // addresses key row e (+ 4h) and features 4g .. 4g + 3 (+ 16 for the upper
+  // 16 lanes of each half-wave)
+  const int vlane = VT ? l32 * VS + 8 * h
+                       : (4 * h + ((l32 & 15) >> 2)) * VS + 16 * (l32 >> 4) + 4 * (l32 & 3);
 
   // the wave's queries as the B operand (k = features 16c + 8h .. +8)
   bf16x8 qf[D / 16];
@@ -408,9 +438,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
 
   const int nk = (it.k1 - it.k0 + BK - 1) / BK;
   constexpr int NT = 64 * NW;
-  StageBF<D, DV, NT> st;
+  StageBF<D, DV, NT, VT> st;
   st.load(Kh + (int64_t)it.k0 * rsk, Vh + (int64_t)it.k0 * rsv, it.k1 - it.k0, rsb, rsbv, tid);
-  st.store(sm.k[0], sm.vt[0], tid);
+  st.store(sm.k[0], sm.v[0], tid);
   if (nk > 1)
     st.load(Kh + (int64_t)(it.k0 + BK) * rsk, Vh + (int64_t)(it.k0 + BK) * rsv,
             it.k1 - it.k0 - BK, rsb, rsbv, tid);
@@ -424,7 +454,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
                         !(window > 0 && wq0 - (kt0 + BK - 1) >= window);
     if (active) {
       const __bf16 *ks = sm.k[buf];
-      const __bf16 *vts = sm.vt[buf];
+      const __bf16 *vs = sm.v[buf];
       const bool full = (kt0 + BK <= it.k1) && (!causal || kt0 + BK - 1 <= wq0) &&
                         (window <= 0 || (wq1 - 1) - kt0 < window);
       bf16x8 a[2][D / 16];
@@ -496,19 +526,30 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
         for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
           for (int e = 0; e < 8; ++e) pf[beta][mm][e] = (__bf16)s[beta][8 * mm + e];
+      // A operand of O^T += V^T P^T: row d = 32 dl + l32 of V^T with the keys
+      // of pf[beta][mm] (32 beta + 16 mm + 4h + 0..3, then the same + 8): one
+      // 16-byte read of the permuted V^T tile, or two transposed reads of the
+      // row-major V tile
 #pragma unroll
       for (int beta = 0; beta < 2; ++beta)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
           for (int dl = 0; dl < DV / 32; ++dl) {
-            const bf16x8 va = *reinterpret_cast<const bf16x8 *>(
-                &vts[(32 * dl + l32) * VS + 32 * beta + 16 * mm + 8 * h]);
+            bf16x8 va;
+            if (VT) {
+              va = *reinterpret_cast<const bf16x8 *>(&vs[vlane + 32 * dl * VS + 32 * beta +
+                                                         16 * mm]);
+            } else {
+              const __bf16 *vp = vs + vlane + (32 * beta + 16 * mm) * VS + 32 * dl;
+              const uint2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 8 * VS);
+              va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+            }
             o[dl] = mfma32x32x16(va, pf[beta][mm], o[dl]);
           }
     }
     if (t + 1 < nk) {
-      st.store(sm.k[buf ^ 1], sm.vt[buf ^ 1], tid);
+      st.store(sm.k[buf ^ 1], sm.v[buf ^ 1], tid);
       if (t + 2 < nk)
         st.load(Kh + (int64_t)(kt0 + 2 * BK) * rsk, Vh + (int64_t)(kt0 + 2 * BK) * rsv,
                 it.k1 - kt0 - 2 * BK, rsb, rsbv, tid);
