@@ -20,11 +20,12 @@
 //              wave), looping over the 64-query tiles that can see it.  S is
 //              formed as Q K^T so that every accumulator lane belongs to one
 //              key; P^T and dS^T then feed the MFMA A operand straight from
-//              registers, and Q^T / dO^T are staged transposed in LDS with the
-//              matching row permutation.
+//              registers, and the Q and dO B operands are read transposed
+//              (ds_read_b64_tr_b16) from the same row-major tiles that serve
+//              S and dP.
 //      dQ:     one block per 128-query tile, looping over key tiles;
-//              S^T = K Q^T as in the forward, K^T staged transposed for
-//              dQ^T = K^T dS^T.
+//              S^T = K Q^T as in the forward, and K^T for dQ^T = K^T dS^T
+//              read transposed from the row-major K tile.
 #include "attn_internal.h"
 #include "device_common.h"
 #include "launch.h"
@@ -61,17 +62,10 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16 *__restrict__ O
   delta[(r % Hs) * Ns + r / Hs] = acc;
 }
 
-// The two bf16 values at position e (0..7) of two 16-byte rows, as one word
-// (first row in the low half).
-__device__ __forceinline__ uint32_t pair_word(const uint4 &a, const uint4 &b, int e) {
-  const uint32_t x[4] = {a.x, a.y, a.z, a.w}, y[4] = {b.x, b.y, b.z, b.w};
-  return (e & 1) ? __byte_perm(x[e / 2], y[e / 2], 0x7632) : __byte_perm(x[e / 2], y[e / 2], 0x5410);
-}
-
 // Stage rows [t0, t0 + 64) of a [slots, Hs, D] tensor (rows >= lim read as
-// zero): `nat` gets the rows as they are (row stride D + 8), `tr` (optional)
-// the transpose with rows permuted by perm16 (row stride 72).  Work unit of a
-// thread: a pair of rows x 8 features.
+// zero) into a row-major LDS tile of row stride D + 8 (the transposed
+// operands are read from it with ds_read_b64_tr_b16).  Work unit of a thread:
+// a pair of rows x 8 features.
 template <int D, int NT>
 struct PairStage {
   static constexpr int UNITS = 32 * (D / 8);
@@ -92,8 +86,8 @@ struct PairStage {
         r[u][e] = buf_load16(rsrc, (uint32_t)(2 * rp + e) * rsb + 16u * c8);
     }
   }
-  __device__ __forceinline__ void store(__bf16 *nat, __bf16 *tr, int tid) const {
-    constexpr int RS = D + 8, TS = 72;
+  __device__ __forceinline__ void store(__bf16 *nat, int tid) const {
+    constexpr int RS = D + 8;
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
       const int id = tid + NT * u;
@@ -101,12 +95,6 @@ struct PairStage {
       const int rp = id % 32, c8 = id / 32;
       *reinterpret_cast<uint4 *>(&nat[(2 * rp) * RS + 8 * c8]) = r[u][0];
       *reinterpret_cast<uint4 *>(&nat[(2 * rp + 1) * RS + 8 * c8]) = r[u][1];
-      if (tr) {
-        const int pos = perm16(2 * rp);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<uint32_t *>(&tr[(8 * c8 + e) * TS + pos]) = pair_word(r[u][0], r[u][1], e);
-      }
     }
   }
 };
@@ -122,6 +110,20 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const __bf16 *p) {
   return *reinterpret_cast<const bf16x8 *>(p);
 }
 
+// MFMA operand with k running down the rows of a row-major bf16 tile (row
+// stride `stride` elements): for lane (l32, h), column n = l32 of the tile
+// (relative to p) and rows 4h + 0..3, then 8 + 4h + 0..3 -- the row order of
+// a 32x32 accumulator's registers 8m .. 8m + 7 -- by two ds_read_b64_tr_b16.
+// Inside each group of 16 lanes, lane 4e + g addresses row e and columns
+// 4g .. 4g + 3 (plus 16 for the upper 16 lanes of each half-wave).
+__device__ __forceinline__ int tr_lane(int h, int l32, int stride) {
+  return (4 * h + ((l32 & 15) >> 2)) * stride + 16 * (l32 >> 4) + 4 * (l32 & 3);
+}
+__device__ __forceinline__ bf16x8 tr_operand(const __bf16 *p, int stride) {
+  const uint2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 8 * stride);
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
 // two blocks per CU only when both widths are 64 (registers and LDS allow it)
 template <int D, int DV>
 constexpr int bwd_min_blocks() {
@@ -133,11 +135,9 @@ constexpr int bwd_min_blocks() {
 // D: width of Q, K (and their gradients); DV: width of V, O, dO, dV.
 template <int D, int DV>
 struct DkvBuf {
-  static constexpr int RS = D + 8, RSV = DV + 8, TS = 72, BQ = kBwdBQ;
+  static constexpr int RS = D + 8, RSV = DV + 8, BQ = kBwdBQ;
   __bf16 q[BQ * RS];
   __bf16 g[BQ * RSV];
-  __bf16 qt[D * TS];
-  __bf16 gt[DV * TS];
   float lse2[BQ];  // LSE * log2(e)
   float dl[BQ];    // -D (the start value of the dP accumulator)
 };
@@ -154,7 +154,7 @@ __device__ __forceinline__ void dkv_item(
     const float *__restrict__ LSE, const float *__restrict__ delta, float *__restrict__ dK,
     float *__restrict__ dV, int Hs, int Hks, int G, int64_t Ns, float scale, float scale_log2,
     int causal, int window) {
-  constexpr int RS = DkvBuf<D, DV>::RS, RSV = DkvBuf<D, DV>::RSV, TS = DkvBuf<D, DV>::TS;
+  constexpr int RS = DkvBuf<D, DV>::RS, RSV = DkvBuf<D, DV>::RSV;
   constexpr int BQ = kBwdBQ;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -170,6 +170,7 @@ __device__ __forceinline__ void dkv_item(
   const int wk0 = it.q0 + 32 * w, wk1 = min(wk0 + 32, it.q1);
   const int kj = wk0 + l32;  // this lane's key (column of S)
   const bool kok = kj < it.q1;
+  const int trl_q = tr_lane(h, l32, RS), trl_g = tr_lane(h, l32, RSV);
 
   bf16x8 kf[D / 16], vf[DV / 16];
 #pragma unroll
@@ -211,8 +212,8 @@ __device__ __forceinline__ void dkv_item(
     }
   };
   auto store_tile = [&](DkvBuf<D, DV> &bf) {
-    sq.store(bf.q, bf.qt, tid);
-    sg.store(bf.g, bf.gt, tid);
+    sq.store(bf.q, tid);
+    sg.store(bf.g, tid);
     if (tid < BQ) bf.lse2[tid] = st_lse;
     else if (tid < 2 * BQ) bf.dl[tid - BQ] = st_lse;
   };
@@ -275,9 +276,15 @@ __device__ __forceinline__ void dkv_item(
       for (int dl = 0; dl < (D > DV ? D : DV) / 32; ++dl)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const int off = (32 * dl + l32) * TS + 32 * rho + 16 * m + 8 * h;
-          if (dl < DV / 32) dv[dl] = mfma32x32x16(pa[m], load_bf16x8(&cur.gt[off]), dv[dl]);
-          if (dl < D / 32) dk[dl] = mfma32x32x16(da[m], load_bf16x8(&cur.qt[off]), dk[dl]);
+          // B operands dO and Q with the query order of pa / da, read
+          // transposed from the row-major tiles
+          const int row = 32 * rho + 16 * m;
+          if (dl < DV / 32)
+            dv[dl] = mfma32x32x16(pa[m], tr_operand(&cur.g[trl_g + row * RSV + 32 * dl], RSV),
+                                  dv[dl]);
+          if (dl < D / 32)
+            dk[dl] = mfma32x32x16(da[m], tr_operand(&cur.q[trl_q + row * RS + 32 * dl], RS),
+                                  dk[dl]);
         }
     }
     }
@@ -314,10 +321,9 @@ __device__ __forceinline__ void dkv_item(
 
 template <int D, int DV>
 struct DqBuf {
-  static constexpr int RS = D + 8, RSV = DV + 8, TS = 72;
+  static constexpr int RS = D + 8, RSV = DV + 8;
   __bf16 k[kFwdBK * RS];
   __bf16 v[kFwdBK * RSV];
-  __bf16 kt[D * TS];
 };
 template <int D, int DV>
 struct DqSmem {
@@ -331,7 +337,7 @@ __device__ __forceinline__ void dq_item(
     const __bf16 *__restrict__ K, const __bf16 *__restrict__ V, const __bf16 *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ delta, float *__restrict__ dQ,
     int Hs, int Hks, int G, int64_t Ns, float scale, float scale_log2, int causal, int window) {
-  constexpr int RS = DqBuf<D, DV>::RS, RSV = DqBuf<D, DV>::RSV, TS = DqBuf<D, DV>::TS;
+  constexpr int RS = DqBuf<D, DV>::RS, RSV = DqBuf<D, DV>::RSV;
   constexpr int BK = kFwdBK;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -346,6 +352,7 @@ __device__ __forceinline__ void dq_item(
   const int wq0 = it.q0 + 32 * w, wq1 = min(wq0 + 32, it.q1);
   const int qi = wq0 + l32;
   const bool qok = qi < it.q1;
+  const int trl_k = tr_lane(h, l32, RS);
 
   bf16x8 qf[D / 16], gf[DV / 16];
 #pragma unroll
@@ -384,8 +391,8 @@ __device__ __forceinline__ void dq_item(
   PairStage<DV, 64 * NW> sv;
   sk.load(K + hk, rsk, it.k0, it.k1, tid);
   sv.load(V + hv, rsv, it.k0, it.k1, tid);
-  sk.store(sm.b[0].k, sm.b[0].kt, tid);
-  sv.store(sm.b[0].v, nullptr, tid);
+  sk.store(sm.b[0].k, tid);
+  sv.store(sm.b[0].v, tid);
   if (nk > 1) {
     sk.load(K + hk, rsk, it.k0 + BK, it.k1, tid);
     sv.load(V + hv, rsv, it.k0 + BK, it.k1, tid);
@@ -435,13 +442,14 @@ __device__ __forceinline__ void dq_item(
       for (int beta = 0; beta < 2; ++beta)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const bf16x8 a = load_bf16x8(&cur.kt[(32 * dl + l32) * TS + 32 * beta + 16 * m + 8 * h]);
+          // K^T rows with the key order of dp, read transposed from the K tile
+          const bf16x8 a = tr_operand(&cur.k[trl_k + (32 * beta + 16 * m) * RS + 32 * dl], RS);
           dq[dl] = mfma32x32x16(a, to_bf16x8(dp[beta], 8 * m), dq[dl]);
         }
     }
     if (t + 1 < nk) {
-      sk.store(sm.b[(t + 1) & 1].k, sm.b[(t + 1) & 1].kt, tid);
-      sv.store(sm.b[(t + 1) & 1].v, nullptr, tid);
+      sk.store(sm.b[(t + 1) & 1].k, tid);
+      sv.store(sm.b[(t + 1) & 1].v, tid);
       if (t + 2 < nk) {
         sk.load(K + hk, rsk, kt0 + 2 * BK, it.k1, tid);
         sv.load(V + hv, rsv, kt0 + 2 * BK, it.k1, tid);
