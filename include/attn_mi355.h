@@ -172,7 +172,7 @@ attn_status attn_plan_stats(const attn_plan *plan, attn_plan_info *info);
  * scheduling analysis.  which = 0: forward items (256 query slots each for
  * bf16; 128 for fp32, for windows of at most 512 slots and when no sequence
  * is longer than 2048 slots); which = 1:
- * backward key-tile items (128 key slots); which = 2: backward dQ items (128
+ * backward key-tile items (256 key slots); which = 2: backward dQ items (256
  * query slots).  The backward lists are empty for fp32 problems.  The head
  * of every item is a query (attention) head; with grouped K/V heads the key
  * tiles of a group's query heads add into the same dK/dV rows.

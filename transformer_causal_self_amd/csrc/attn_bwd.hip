@@ -16,14 +16,14 @@
 //   1. delta:  D_i for every (attention head, slot).
 //   2. one grid of two item kinds (the dQ items fill the CUs that the dK/dV
 //      tail leaves idle):
-//      dK/dV:  one block per 128-key tile of one attention head (32 keys per
+//      dK/dV:  one block per 256-key tile of one attention head (32 keys per
 //              wave), looping over the 64-query tiles that can see it.  S is
 //              formed as Q K^T so that every accumulator lane belongs to one
 //              key; P^T and dS^T then feed the MFMA A operand straight from
 //              registers, and the Q and dO B operands are read transposed
 //              (ds_read_b64_tr_b16) from the same row-major tiles that serve
 //              S and dP.
-//      dQ:     one block per 128-query tile, looping over key tiles;
+//      dQ:     one block per 256-query tile, looping over key tiles;
 //              S^T = K Q^T as in the forward, and K^T for dQ^T = K^T dS^T
 //              read transposed from the row-major K tile.
 #include "attn_internal.h"

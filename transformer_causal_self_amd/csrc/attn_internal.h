@@ -25,11 +25,11 @@ constexpr int kFwdShortSeq = 2048;    // and so do problems whose sequences all 
 constexpr int kFwdBQF32 = 128;
 constexpr int kFwdThreadsF32 = 256;
 constexpr int kFwdBK = 64;
-//   backward: both passes run four waves of 32 rows (keys for dK/dV, queries
-//   for dQ) per work item and step over 64 partner rows at a time.  (Eight
-//   waves per item, which halves the staging per row, measured slower here:
-//   one block per CU instead of two.)
-constexpr int kBwdWaves = 4;
+//   backward: both passes run eight waves of 32 rows (keys for dK/dV, queries
+//   for dQ) per work item and step over 64 partner rows at a time: each
+//   staged partner tile serves 256 rows (four waves per item measured 11-12%
+//   slower at d = 128 and 1% at d = 64).
+constexpr int kBwdWaves = 8;
 constexpr int kBwdRows = 32 * kBwdWaves;
 constexpr int kBwdBQ = 64;
 //   rotary: threads per block, and the fine step of the two-level cos/sin
