@@ -11,19 +11,20 @@
 // tiling changes where the result is computed, not the result).
 //
 // gfx950 mapping (one work item = one block of 8 waves = 256 query slots of
-// one attention head for bf16, 4 waves = 128 slots for fp32 and for windows of
-// at most 512 slots; each wave owns 32 query slots, and every K/V tile staged
-// in LDS serves the whole block):
+// one attention head for bf16, 4 waves = 128 slots for fp32, for windows of
+// at most 512 slots and when every sequence fits 2048 slots; each wave owns
+// 32 query slots, and every K/V tile staged in LDS serves the whole block):
 //   * Each wave holds its 32 queries as the B operand of
 //     v_mfma_f32_32x32x16_bf16 for the whole item (registers).
-//   * K tiles of 64 key slots are staged in LDS row-major; V tiles are staged
-//     transposed (V^T, d-major) so both PV operands are k-contiguous.
+//   * K tiles of 64 key slots are staged in LDS row-major.  V tiles are staged
+//     transposed (V^T, d-major) for eight-wave items, row-major for four-wave
+//     items, which read V^T with ds_read_b64_tr_b16 (see SmemBF).
 //   * S^T = K Q^T: with keys as MFMA rows and queries as columns, every lane of
 //     the accumulator holds one query's scores, so the row max and row sum are
 //     in-lane reductions plus one exchange between the two half-waves.
 //   * P^T goes straight from the accumulator registers to the B operand of
-//     O^T += V^T P^T (no LDS round trip): the V^T tile's key columns are stored
-//     in the order in which the accumulator holds them (bits 2 and 3 of the key
+//     O^T += V^T P^T (no LDS round trip): V^T is read with its keys in the
+//     order in which the accumulator holds them (bits 2 and 3 of the key
 //     index swapped inside each group of 16).
 //   * exp uses v_exp_f32 (2^x) with log2(e) folded into the scale; masking is
 //     applied only on tiles that cross the causal diagonal, the window edge or
