@@ -200,10 +200,13 @@ __device__ __forceinline__ void dkv_item(
   const int nq = (it.k1 - it.k0 + BQ - 1) / BQ;
   PairStage<D, 64 * NW> sq;
   PairStage<DV, 64 * NW> sg;
+  // a 64-wide tile has fewer staging units than the block has threads: the
+  // dO tile goes to the other half of the block than the Q tile
+  const int tid_g = (tid + 32 * NW) % (64 * NW);
   float st_lse = 0.0f;
   auto load_tile = [&](int q0) {
     sq.load(Q + ho, rs, q0, it.k1, tid);
-    sg.load(dO + hoo, rso, q0, it.k1, tid);
+    sg.load(dO + hoo, rso, q0, it.k1, tid_g);
     if (tid < 2 * BQ) {
       const int row = q0 + (tid % BQ);
       st_lse = row < it.k1 ? (tid < BQ ? LSE[(int64_t)it.head * Ns + row] * kLog2e
@@ -213,7 +216,7 @@ __device__ __forceinline__ void dkv_item(
   };
   auto store_tile = [&](DkvBuf<D, DV> &bf) {
     sq.store(bf.q, tid);
-    sg.store(bf.g, tid);
+    sg.store(bf.g, tid_g);
     if (tid < BQ) bf.lse2[tid] = st_lse;
     else if (tid < 2 * BQ) bf.dl[tid - BQ] = st_lse;
   };
@@ -389,13 +392,14 @@ __device__ __forceinline__ void dq_item(
   const int nk = (it.k1 - it.k0 + BK - 1) / BK;
   PairStage<D, 64 * NW> sk;
   PairStage<DV, 64 * NW> sv;
+  const int tid_v = (tid + 32 * NW) % (64 * NW);  // V staged by the other half
   sk.load(K + hk, rsk, it.k0, it.k1, tid);
-  sv.load(V + hv, rsv, it.k0, it.k1, tid);
+  sv.load(V + hv, rsv, it.k0, it.k1, tid_v);
   sk.store(sm.b[0].k, tid);
-  sv.store(sm.b[0].v, tid);
+  sv.store(sm.b[0].v, tid_v);
   if (nk > 1) {
     sk.load(K + hk, rsk, it.k0 + BK, it.k1, tid);
-    sv.load(V + hv, rsv, it.k0 + BK, it.k1, tid);
+    sv.load(V + hv, rsv, it.k0 + BK, it.k1, tid_v);
   }
   __syncthreads();
   for (int t = 0; t < nk; ++t) {
@@ -449,10 +453,10 @@ __device__ __forceinline__ void dq_item(
     }
     if (t + 1 < nk) {
       sk.store(sm.b[(t + 1) & 1].k, tid);
-      sv.store(sm.b[(t + 1) & 1].v, tid);
+      sv.store(sm.b[(t + 1) & 1].v, tid_v);
       if (t + 2 < nk) {
         sk.load(K + hk, rsk, kt0 + 2 * BK, it.k1, tid);
-        sv.load(V + hv, rsv, kt0 + 2 * BK, it.k1, tid);
+        sv.load(V + hv, rsv, kt0 + 2 * BK, it.k1, tid_v);
       }
     }
     __syncthreads();
