@@ -149,7 +149,9 @@ typedef struct {
  * no HIP call.  On success *out owns a plan to free with attn_plan_destroy.
  * Errors: ATTN_E_INVALID (bad field), ATTN_E_UNSUPPORTED (head_dim or
  * v_head_dim not 64 or 128; v_head_dim != head_dim with fp32; grouped K/V
- * heads with pairing), ATTN_E_NOMEM.
+ * heads with pairing; num_heads * max(head_dim, v_head_dim) above 2^20,
+ * which keeps the byte offsets inside a 256-slot tile in 31 bits),
+ * ATTN_E_NOMEM.
  */
 attn_status attn_plan_create(const attn_problem *problem, attn_plan **out);
 

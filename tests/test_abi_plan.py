@@ -75,11 +75,19 @@ def plan(**kw):
     (dict(v_head_dim=63), -1),
     (dict(v_head_dim=96), -2),                         # value width not covered
     (dict(v_head_dim=128, dtype="fp32"), -2),          # separate value width: bf16 only
+    (dict(num_heads=8194, head_dim=128), -2),          # tile offsets would pass 2^31
+    (dict(num_heads=16386, head_dim=64, paired=1), -2),
+    (dict(num_heads=16386, num_kv_heads=2, v_head_dim=128), -2),
 ])
 def test_plan_rejects(kw, status):
     with pytest.raises(tca.AttnError) as e:
         plan(**kw)
     assert e.value.status == status
+
+
+def test_head_count_limit_is_inclusive():
+    assert plan(num_heads=8192, head_dim=128).info["attn_heads"] == 8192
+    assert plan(num_heads=16384, head_dim=64).info["attn_heads"] == 16384
 
 
 @pytest.mark.parametrize("d,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])

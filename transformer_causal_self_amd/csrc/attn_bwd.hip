@@ -26,6 +26,10 @@
 //      dQ:     one block per 256-query tile, looping over key tiles;
 //              S^T = K Q^T as in the forward, and K^T for dQ^T = K^T dS^T
 //              read transposed from the row-major K tile.
+//   The streamed tiles (Q, dO; K, V) go from global memory straight into LDS
+//   (buffer loads with the LDS flag), double buffered: the next tile's loads
+//   are issued before the current tile's MMAs and waited for after them, and
+//   no staging register or LDS store instruction is spent on them.
 #include "attn_internal.h"
 #include "device_common.h"
 #include "launch.h"
@@ -62,42 +66,28 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16 *__restrict__ O
   delta[(r % Hs) * Ns + r / Hs] = acc;
 }
 
-// Stage rows [t0, t0 + 64) of a [slots, Hs, D] tensor (rows >= lim read as
-// zero) into a row-major LDS tile of row stride D + 8 (the transposed
-// operands are read from it with ds_read_b64_tr_b16).  Work unit of a thread:
-// a pair of rows x 8 features.
-template <int D, int NT>
-struct PairStage {
-  static constexpr int UNITS = 32 * (D / 8);
-  static constexpr int PT = (UNITS + NT - 1) / NT;  // units per thread (NT threads)
-  uint4 r[PT][2];
-  // rows [t0, t0 + 64) of the head whose first slot is `base`; rows at or past
-  // `lim` read zero (the buffer resource ends there)
-  __device__ __forceinline__ void load(const __bf16 *base, int64_t rs, int t0, int lim, int tid) {
-    const uint32_t rsb = (uint32_t)rs * 2u;
-    const auto rsrc = make_rsrc(base + (int64_t)t0 * rs, (uint32_t)max(0, min(lim - t0, 64)) * rsb);
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int id = tid + NT * u;
-      if (UNITS % NT != 0 && id >= UNITS) break;
-      const int rp = id % 32, c8 = id / 32;
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        r[u][e] = buf_load16(rsrc, (uint32_t)(2 * rp + e) * rsb + 16u * c8);
-    }
-  }
-  __device__ __forceinline__ void store(__bf16 *nat, int tid) const {
-    constexpr int RS = D + 8;
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int id = tid + NT * u;
-      if (UNITS % NT != 0 && id >= UNITS) break;
-      const int rp = id % 32, c8 = id / 32;
-      *reinterpret_cast<uint4 *>(&nat[(2 * rp) * RS + 8 * c8]) = r[u][0];
-      *reinterpret_cast<uint4 *>(&nat[(2 * rp + 1) * RS + 8 * c8]) = r[u][1];
-    }
+// Direct global -> LDS staging (buffer_load_dwordx4 with the LDS flag) of
+// the 64 rows [t0, t0 + 64) of a [slots, heads, W] bf16 tensor into a
+// row-major LDS tile of row stride W + 8 elements.  A wave instruction writes
+// 1 KB of LDS, lane L at byte 16 L, so instruction i fills the padded tile's
+// 16-byte chunks [64 i, 64 i + 64); a lane whose chunk is a row's pad, or
+// whose row is past the buffer resource's end, reads out of range, which
+// writes zeros.
+template <int W>
+struct DmaTile {
+  static constexpr int RC = W / 8 + 1;  // 16-byte chunks per LDS row, the last one pad
+  static constexpr int NI = RC;         // wave instructions per 64-row tile
+  __device__ static __forceinline__ uint32_t offset(int i, int lane, uint32_t rsb) {
+    const int p = 64 * i + lane, row = p / RC, c = p % RC;
+    return c < W / 8 ? (uint32_t)row * rsb + 16u * (uint32_t)c : 0x80000000u;
   }
 };
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, __bf16 *lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
+                                           off, 0, 0, 0);
+}
+// wait for this wave's staging loads (vmcnt 0; other counters left alone)
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ bf16x8 to_bf16x8(const floatx16 &x, int first) {
   bf16x8 r;
@@ -198,15 +188,23 @@ __device__ __forceinline__ void dkv_item(
   for (int dl = 0; dl < D / 32; ++dl) dk[dl] = floatx16{};
 
   const int nq = (it.k1 - it.k0 + BQ - 1) / BQ;
-  PairStage<D, 64 * NW> sq;
-  PairStage<DV, 64 * NW> sg;
-  // a 64-wide tile has fewer staging units than the block has threads: the
-  // dO tile goes to the other half of the block than the Q tile
-  const int tid_g = (tid + 32 * NW) % (64 * NW);
+  static_assert(BQ == 64, "one DMA instruction per 64-row chunk column");
+  const uint32_t rsb = (uint32_t)rs * 2u, rsbo = (uint32_t)rso * 2u;
   float st_lse = 0.0f;
-  auto load_tile = [&](int q0) {
-    sq.load(Q + ho, rs, q0, it.k1, tid);
-    sg.load(dO + hoo, rso, q0, it.k1, tid_g);
+  // start the loads of query tile q0 into bf (Q, dO straight into LDS; the
+  // LSE / -D values into a register)
+  auto issue = [&](DkvBuf<D, DV> &bf, int q0) {
+    const uint32_t n = (uint32_t)max(0, min(it.k1 - q0, BQ));
+    const auto rq = make_rsrc(Q + ho + (int64_t)q0 * rs, n * rsb);
+    const auto rg = make_rsrc(dO + hoo + (int64_t)q0 * rso, n * rsbo);
+    constexpr int NQ = DmaTile<D>::NI, NG = DmaTile<DV>::NI;
+#pragma unroll
+    for (int j0 = 0; j0 < NQ + NG; j0 += NW) {
+      const int j = j0 + w;
+      if (j < NQ) dma16(rq, &bf.q[512 * j], DmaTile<D>::offset(j, lane, rsb));
+      else if (j < NQ + NG)
+        dma16(rg, &bf.g[512 * (j - NQ)], DmaTile<DV>::offset(j - NQ, lane, rsbo));
+    }
     if (tid < 2 * BQ) {
       const int row = q0 + (tid % BQ);
       st_lse = row < it.k1 ? (tid < BQ ? LSE[(int64_t)it.head * Ns + row] * kLog2e
@@ -214,19 +212,19 @@ __device__ __forceinline__ void dkv_item(
                            : 0.0f;
     }
   };
-  auto store_tile = [&](DkvBuf<D, DV> &bf) {
-    sq.store(bf.q, tid);
-    sg.store(bf.g, tid_g);
+  // store the register part and wait for this wave's LDS loads
+  auto finish = [&](DkvBuf<D, DV> &bf) {
     if (tid < BQ) bf.lse2[tid] = st_lse;
     else if (tid < 2 * BQ) bf.dl[tid - BQ] = st_lse;
+    wait_dma();
   };
-  load_tile(it.k0);
-  store_tile(sm.b[0]);
-  if (nq > 1) load_tile(it.k0 + BQ);
+  issue(sm.b[0], it.k0);
+  finish(sm.b[0]);
   __syncthreads();
   for (int t = 0; t < nq; ++t) {
     const int qt0 = it.k0 + t * BQ;
     const DkvBuf<D, DV> &cur = sm.b[t & 1];
+    if (t + 1 < nq) issue(sm.b[(t + 1) & 1], qt0 + BQ);
     const int qt1 = min(qt0 + BQ, it.k1);  // one past the last valid query
     const bool active = wk0 < wk1 && !(causal && qt1 - 1 < wk0) &&
                         !(window > 0 && qt0 - (wk1 - 1) >= window);
@@ -291,10 +289,7 @@ __device__ __forceinline__ void dkv_item(
         }
     }
     }
-    if (t + 1 < nq) {
-      store_tile(sm.b[(t + 1) & 1]);
-      if (t + 2 < nq) load_tile(qt0 + 2 * BQ);
-    }
+    if (t + 1 < nq) finish(sm.b[(t + 1) & 1]);
     __syncthreads();
   }
   // epilogue: accumulator rows are keys 8b + 4h + i of the wave, columns d
@@ -390,21 +385,29 @@ __device__ __forceinline__ void dq_item(
   for (int dl = 0; dl < D / 32; ++dl) dq[dl] = floatx16{};
 
   const int nk = (it.k1 - it.k0 + BK - 1) / BK;
-  PairStage<D, 64 * NW> sk;
-  PairStage<DV, 64 * NW> sv;
-  const int tid_v = (tid + 32 * NW) % (64 * NW);  // V staged by the other half
-  sk.load(K + hk, rsk, it.k0, it.k1, tid);
-  sv.load(V + hv, rsv, it.k0, it.k1, tid_v);
-  sk.store(sm.b[0].k, tid);
-  sv.store(sm.b[0].v, tid_v);
-  if (nk > 1) {
-    sk.load(K + hk, rsk, it.k0 + BK, it.k1, tid);
-    sv.load(V + hv, rsv, it.k0 + BK, it.k1, tid_v);
-  }
+  static_assert(BK == 64, "one DMA instruction per 64-row chunk column");
+  const uint32_t rsbk = (uint32_t)rsk * 2u, rsbv = (uint32_t)rsv * 2u;
+  // start the loads of key tile k0 into bf (K, V straight into LDS)
+  auto issue = [&](DqBuf<D, DV> &bf, int k0) {
+    const uint32_t n = (uint32_t)max(0, min(it.k1 - k0, BK));
+    const auto rk = make_rsrc(K + hk + (int64_t)k0 * rsk, n * rsbk);
+    const auto rv = make_rsrc(V + hv + (int64_t)k0 * rsv, n * rsbv);
+    constexpr int NK = DmaTile<D>::NI, NV = DmaTile<DV>::NI;
+#pragma unroll
+    for (int j0 = 0; j0 < NK + NV; j0 += NW) {
+      const int j = j0 + w;
+      if (j < NK) dma16(rk, &bf.k[512 * j], DmaTile<D>::offset(j, lane, rsbk));
+      else if (j < NK + NV)
+        dma16(rv, &bf.v[512 * (j - NK)], DmaTile<DV>::offset(j - NK, lane, rsbv));
+    }
+  };
+  issue(sm.b[0], it.k0);
+  wait_dma();
   __syncthreads();
   for (int t = 0; t < nk; ++t) {
     const int kt0 = it.k0 + t * BK;
     const DqBuf<D, DV> &cur = sm.b[t & 1];
+    if (t + 1 < nk) issue(sm.b[(t + 1) & 1], kt0 + BK);
     const bool active = wq0 < wq1 && !(causal && kt0 > wq1 - 1) &&
                         !(window > 0 && wq0 - (kt0 + BK - 1) >= window);
     if (active) {
@@ -451,14 +454,7 @@ __device__ __forceinline__ void dq_item(
           dq[dl] = mfma32x32x16(a, to_bf16x8(dp[beta], 8 * m), dq[dl]);
         }
     }
-    if (t + 1 < nk) {
-      sk.store(sm.b[(t + 1) & 1].k, tid);
-      sv.store(sm.b[(t + 1) & 1].v, tid_v);
-      if (t + 2 < nk) {
-        sk.load(K + hk, rsk, kt0 + 2 * BK, it.k1, tid);
-        sv.load(V + hv, rsv, kt0 + 2 * BK, it.k1, tid_v);
-      }
-    }
+    if (t + 1 < nk) wait_dma();
     __syncthreads();
   }
   if (qok) {

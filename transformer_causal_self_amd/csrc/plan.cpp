@@ -180,6 +180,10 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
   if (dv != 64 && dv != 128) return ATTN_E_UNSUPPORTED;
   if (dv != pr->head_dim && pr->dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
   if (Hkv != pr->num_heads && pr->paired) return ATTN_E_UNSUPPORTED;
+  // tiles of up to 256 slots are addressed by 32-bit byte offsets, with an
+  // offset of 2^31 standing for "out of range"
+  if ((int64_t)pr->num_heads * std::max(pr->head_dim, dv) > (int64_t(1) << 20))
+    return ATTN_E_UNSUPPORTED;
 
   attn_plan *p = new (std::nothrow) attn_plan();
   if (!p) return ATTN_E_NOMEM;
