@@ -66,29 +66,6 @@ __global__ __launch_bounds__(256) void delta_kernel(const __bf16 *__restrict__ O
   delta[(r % Hs) * Ns + r / Hs] = acc;
 }
 
-// Direct global -> LDS staging (buffer_load_dwordx4 with the LDS flag) of
-// the 64 rows [t0, t0 + 64) of a [slots, heads, W] bf16 tensor into a
-// row-major LDS tile of row stride W + 8 elements.  A wave instruction writes
-// 1 KB of LDS, lane L at byte 16 L, so instruction i fills the padded tile's
-// 16-byte chunks [64 i, 64 i + 64); a lane whose chunk is a row's pad, or
-// whose row is past the buffer resource's end, reads out of range, which
-// writes zeros.
-template <int W>
-struct DmaTile {
-  static constexpr int RC = W / 8 + 1;  // 16-byte chunks per LDS row, the last one pad
-  static constexpr int NI = RC;         // wave instructions per 64-row tile
-  __device__ static __forceinline__ uint32_t offset(int i, int lane, uint32_t rsb) {
-    const int p = 64 * i + lane, row = p / RC, c = p % RC;
-    return c < W / 8 ? (uint32_t)row * rsb + 16u * (uint32_t)c : 0x80000000u;
-  }
-};
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, __bf16 *lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
-                                           off, 0, 0, 0);
-}
-// wait for this wave's staging loads (vmcnt 0; other counters left alone)
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
 __device__ __forceinline__ bf16x8 to_bf16x8(const floatx16 &x, int first) {
   bf16x8 r;
 #pragma unroll
