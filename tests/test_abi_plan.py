@@ -114,15 +114,18 @@ def test_empty_problem_is_valid():
 
 def test_item_sizes_follow_the_dtype():
     # bf16: 256-query forward items, 256-row backward dK/dV (keys) and dQ
-    # (queries) items; fp32 (no backward): 128-query forward items and empty
-    # backward lists
+    # (queries) items (128 rows when both widths are 64); fp32 (no backward):
+    # 128-query forward items and empty backward lists
     cu = [0, 2100]
     pb = plan(num_tokens=2100, cu_seqlens=cu)
     pb128 = plan(num_tokens=2100, cu_seqlens=cu, head_dim=128)
     pf = plan(num_tokens=2100, cu_seqlens=cu, dtype="fp32")
     rows = lambda p, which: np.diff(p.work_items(which)[:, 1:3], axis=1).max()
-    assert rows(pb, 0) == 256 and rows(pb, 1) == 256 and rows(pb, 2) == 256
+    assert rows(pb, 0) == 256 and rows(pb, 1) == 128 and rows(pb, 2) == 128
     assert rows(pb128, 0) == 256 and rows(pb128, 1) == 256 and rows(pb128, 2) == 256
+    for d, dv in ((64, 128), (128, 64)):
+        pm = plan(num_tokens=2100, cu_seqlens=cu, head_dim=d, v_head_dim=dv)
+        assert rows(pm, 1) == 256 and rows(pm, 2) == 256
     assert rows(pf, 0) == 128
     # a short window keeps 128-query forward items (a longer one does not)
     assert np.diff(plan(num_tokens=2100, cu_seqlens=cu, window=512).work_items(0)[:, 1:3],

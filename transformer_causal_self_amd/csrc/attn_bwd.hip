@@ -17,13 +17,15 @@
 //   2. one grid of two item kinds (the dQ items fill the CUs that the dK/dV
 //      tail leaves idle):
 //      dK/dV:  one block per 256-key tile of one attention head (32 keys per
-//              wave), looping over the 64-query tiles that can see it.  S is
+//              wave; 128-key tiles on four waves when both widths are 64),
+//              looping over the 64-query tiles that can see it.  S is
 //              formed as Q K^T so that every accumulator lane belongs to one
 //              key; P^T and dS^T then feed the MFMA A operand straight from
 //              registers, and the Q and dO B operands are read transposed
 //              (ds_read_b64_tr_b16) from the same row-major tiles that serve
 //              S and dP.
-//      dQ:     one block per 256-query tile, looping over key tiles;
+//      dQ:     one block per 256-query tile (128 when both widths are 64),
+//              looping over key tiles;
 //              S^T = K Q^T as in the forward, and K^T for dQ^T = K^T dS^T
 //              read transposed from the row-major K tile.
 //   The streamed tiles (Q, dO; K, V) go from global memory straight into LDS
@@ -91,10 +93,21 @@ __device__ __forceinline__ bf16x8 tr_operand(const __bf16 *p, int stride) {
   return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
-// two blocks per CU only when both widths are 64 (registers and LDS allow it)
+// waves per SIMD the register budget is sized for: three four-wave blocks
+// per CU when both widths are 64 (at most 168 VGPRs), else one eight-wave
+// block (two waves per SIMD, 256 VGPRs)
 template <int D, int DV>
-constexpr int bwd_min_blocks() {
-  return D == 64 && DV == 64 ? 2 : 1;
+constexpr int bwd_waves_per_simd() {
+  return D == 64 && DV == 64 ? 3 : 2;
+}
+
+// With both widths 64, a wave raises its issue priority while it issues the
+// S and dP MFMAs, so that the matrix unit is fed while the other wave of the
+// SIMD computes its exponentials (-2.5% backward time at d = 64; at d = 128,
+// where the dK/dV registers are already short, it costs 10-13%).
+template <int D, int DV, int LEVEL>
+__device__ __forceinline__ void mfma_priority() {
+  if constexpr (D == 64 && DV == 64) __builtin_amdgcn_s_setprio(LEVEL);
 }
 
 // ---------------------------------------------------------------- dK, dV --
@@ -226,12 +239,14 @@ __device__ __forceinline__ void dkv_item(
         dp[4 * b + 3] = d4.w;
       }
       // S first: its exponentials can start while dP is multiplied
+      mfma_priority<D, DV, 1>();
 #pragma unroll
       for (int c = 0; c < D / 16; ++c)
         s = mfma32x32x16(load_bf16x8(&cur.q[(32 * rho + l32) * RS + 16 * c + 8 * h]), kf[c], s);
 #pragma unroll
       for (int c = 0; c < DV / 16; ++c)
         dp = mfma32x32x16(load_bf16x8(&cur.g[(32 * rho + l32) * RSV + 16 * c + 8 * h]), vf[c], dp);
+      mfma_priority<D, DV, 0>();
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const float4 l4 = *reinterpret_cast<const float4 *>(&cur.lse2[32 * rho + 8 * b + 4 * h]);
@@ -400,6 +415,7 @@ __device__ __forceinline__ void dq_item(
     for (int beta = 0; beta < 2; ++beta) {
       s[beta] = floatx16{};
       dp[beta] = negd;
+      mfma_priority<D, DV, 1>();
 #pragma unroll
       for (int c = 0; c < D / 16; ++c)
         s[beta] = mfma32x32x16(load_bf16x8(&cur.k[(32 * beta + l32) * RS + 16 * c + 8 * h]), qf[c],
@@ -408,6 +424,7 @@ __device__ __forceinline__ void dq_item(
       for (int c = 0; c < DV / 16; ++c)
         dp[beta] = mfma32x32x16(load_bf16x8(&cur.v[(32 * beta + l32) * RSV + 16 * c + 8 * h]),
                                 gf[c], dp[beta]);
+      mfma_priority<D, DV, 0>();
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[beta][r] = fast_exp2(fmaf(s[beta][r], scale_log2, -lse2));
       if (!full) {  // tiles on the diagonal, the window edge or the range end
@@ -450,7 +467,7 @@ __device__ __forceinline__ void dq_item(
 // the dQ items, so the dQ work fills the CUs the dK/dV tail leaves idle.  The
 // two share one LDS allocation (the larger of the two layouts).
 template <int D, int DV, int NW>
-__global__ __launch_bounds__(64 * NW, (bwd_min_blocks<D, DV>())) void bwd_kernel(
+__global__ __launch_bounds__(64 * NW, (bwd_waves_per_simd<D, DV>())) void bwd_kernel(
     const WorkItem *__restrict__ dkv_items, int n_dkv, const WorkItem *__restrict__ dq_items,
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
     const __bf16 *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ delta,
@@ -491,7 +508,7 @@ hipError_t launch_typed(const attn_plan *p, const void *q, const void *k, const 
   const __bf16 *V = static_cast<const __bf16 *>(v), *O = static_cast<const __bf16 *>(o);
   const __bf16 *G = static_cast<const __bf16 *>(d_o);
   const int64_t rows = Ns * Hs;
-  constexpr int NWK = kBwdWaves, NWQ = kBwdWaves;
+  constexpr int NWK = bwd_waves(D, DV), NWQ = NWK;
   hipLaunchKernelGGL((delta_kernel<DV>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
                      stream, O, G, delta, Hs, Ns);
   if (p->p.G > 1) {

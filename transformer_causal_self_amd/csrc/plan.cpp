@@ -263,6 +263,7 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
       }
       for (auto &v : parts) v.clear();
     };
+    const int bwd_rows = 32 * attn::bwd_waves(P.d, P.dv);  // backward item rows
     for (int kh = 0; kh < P.Hks; ++kh)
       for (int s = 0; s < S; ++s) {
         const int64_t b = (int64_t)cu[s] * mult, e = (int64_t)cu[s + 1] * mult;
@@ -272,8 +273,8 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
           pairs += visible_pairs_of(e - b, P.causal, P.window);
           cut_items(tf[g], j, stream, b, e, p->fwd_bq, P.causal, P.window, true);
           if (bf16) {
-            cut_items(tq[g], j, stream, b, e, attn::kBwdRows, P.causal, P.window, true);
-            cut_items(tb[g], j, stream, b, e, attn::kBwdRows, P.causal, P.window, false);
+            cut_items(tq[g], j, stream, b, e, bwd_rows, P.causal, P.window, true);
+            cut_items(tb[g], j, stream, b, e, bwd_rows, P.causal, P.window, false);
           }
         }
         interleave(tf, p->fwd);
