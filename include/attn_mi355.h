@@ -174,9 +174,8 @@ attn_status attn_plan_stats(const attn_plan *plan, attn_plan_info *info);
  * scheduling analysis.  which = 0: forward items (256 query slots each for
  * bf16; 128 for fp32, for windows of at most 512 slots and when no sequence
  * is longer than 2048 slots); which = 1:
- * backward key-tile items (256 key slots; 128 when head_dim and v_head_dim
- * are both 64); which = 2: backward dQ items (256 query slots; 128 when both
- * widths are 64).  The backward lists are empty for fp32 problems.  The head
+ * backward key-tile items (128 key slots); which = 2: backward dQ items (128
+ * query slots).  The backward lists are empty for fp32 problems.  The head
  * of every item is a query (attention) head; with grouped K/V heads the key
  * tiles of a group's query heads add into the same dK/dV rows.
  * Each item is 8 int32: {attention head, r0, r1, s0, s1, stream, 0, 0}

@@ -113,19 +113,19 @@ def test_empty_problem_is_valid():
 
 
 def test_item_sizes_follow_the_dtype():
-    # bf16: 256-query forward items, 256-row backward dK/dV (keys) and dQ
-    # (queries) items (128 rows when both widths are 64); fp32 (no backward):
-    # 128-query forward items and empty backward lists
+    # bf16: 256-query forward items, 128-row backward dK/dV (keys) and dQ
+    # (queries) items; fp32 (no backward): 128-query forward items and empty
+    # backward lists
     cu = [0, 2100]
     pb = plan(num_tokens=2100, cu_seqlens=cu)
     pb128 = plan(num_tokens=2100, cu_seqlens=cu, head_dim=128)
     pf = plan(num_tokens=2100, cu_seqlens=cu, dtype="fp32")
     rows = lambda p, which: np.diff(p.work_items(which)[:, 1:3], axis=1).max()
     assert rows(pb, 0) == 256 and rows(pb, 1) == 128 and rows(pb, 2) == 128
-    assert rows(pb128, 0) == 256 and rows(pb128, 1) == 256 and rows(pb128, 2) == 256
+    assert rows(pb128, 0) == 256 and rows(pb128, 1) == 128 and rows(pb128, 2) == 128
     for d, dv in ((64, 128), (128, 64)):
         pm = plan(num_tokens=2100, cu_seqlens=cu, head_dim=d, v_head_dim=dv)
-        assert rows(pm, 1) == 256 and rows(pm, 2) == 256
+        assert rows(pm, 1) == 128 and rows(pm, 2) == 128
     assert rows(pf, 0) == 128
     # a short window keeps 128-query forward items (a longer one does not)
     assert np.diff(plan(num_tokens=2100, cu_seqlens=cu, window=512).work_items(0)[:, 1:3],
@@ -207,7 +207,7 @@ def test_counts_and_work_lists_cover_the_mask(cu, H, paired, causal, window):
     def seq_of(slot):
         s = np.searchsorted(bounds, slot, side="right") - 1
         return bounds[s], bounds[s + 1]
-    for lst, rows_max in ((fwd, 256), (dq, 256)):
+    for lst, rows_max in ((fwd, 256), (dq, 128)):
         seen = np.zeros((Hs, N * mult), dtype=int)
         for head, q0, q1, k0, k1, *_ in lst:
             assert 0 < q1 - q0 <= rows_max
@@ -221,7 +221,7 @@ def test_counts_and_work_lists_cover_the_mask(cu, H, paired, causal, window):
     # backward: every (head, key) column exactly once; the queries that see it in [s0, s1)
     seen = np.zeros((Hs, N * mult), dtype=int)
     for head, r0, r1, s0, s1, *_ in bwd:
-        assert 0 < r1 - r0 <= 256
+        assert 0 < r1 - r0 <= 128
         seen[head, r0:r1] += 1
         cols = mask[:, r0:r1]
         rows = np.nonzero(cols.any(axis=1))[0]

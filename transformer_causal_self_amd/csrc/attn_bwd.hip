@@ -16,16 +16,15 @@
 //   1. delta:  D_i for every (attention head, slot).
 //   2. one grid of two item kinds (the dQ items fill the CUs that the dK/dV
 //      tail leaves idle):
-//      dK/dV:  one block per 256-key tile of one attention head (32 keys per
-//              wave; 128-key tiles on four waves when both widths are 64),
-//              looping over the 64-query tiles that can see it.  S is
+//      dK/dV:  one block per 128-key tile of one attention head (four
+//              waves, 32 keys each), looping over the 64-query tiles that
+//              can see it.  S is
 //              formed as Q K^T so that every accumulator lane belongs to one
 //              key; P^T and dS^T then feed the MFMA A operand straight from
 //              registers, and the Q and dO B operands are read transposed
 //              (ds_read_b64_tr_b16) from the same row-major tiles that serve
 //              S and dP.
-//      dQ:     one block per 256-query tile (128 when both widths are 64),
-//              looping over key tiles;
+//      dQ:     one block per 128-query tile, looping over key tiles;
 //              S^T = K Q^T as in the forward, and K^T for dQ^T = K^T dS^T
 //              read transposed from the row-major K tile.
 //   The streamed tiles (Q, dO; K, V) go from global memory straight into LDS
@@ -94,8 +93,7 @@ __device__ __forceinline__ bf16x8 tr_operand(const __bf16 *p, int stride) {
 }
 
 // waves per SIMD the register budget is sized for: three four-wave blocks
-// per CU when both widths are 64 (at most 168 VGPRs), else one eight-wave
-// block (two waves per SIMD, 256 VGPRs)
+// per CU when both widths are 64 (at most 168 VGPRs), else two (256 VGPRs)
 template <int D, int DV>
 constexpr int bwd_waves_per_simd() {
   return D == 64 && DV == 64 ? 3 : 2;
@@ -151,6 +149,10 @@ __device__ __forceinline__ void dkv_item(
   const int kj = wk0 + l32;  // this lane's key (column of S)
   const bool kok = kj < it.q1;
   const int trl_q = tr_lane(h, l32, RS), trl_g = tr_lane(h, l32, RSV);
+  // with a width of 128 the two 32-query halves of a tile run one after the
+  // other (no overlap): the registers hold only one half's S and dP next to
+  // the dK/dV accumulators (fewer spills, 2-10% faster)
+  constexpr int RHO_UNROLL = D == 64 && DV == 64 ? 2 : 1;
 
   bf16x8 kf[D / 16], vf[DV / 16];
 #pragma unroll
@@ -225,7 +227,7 @@ __device__ __forceinline__ void dkv_item(
     // lane's key itself may be past the item end -- its column is never stored
     const int qlo = causal ? kj - qt0 : -(1 << 30);
     const int qhi = min(it.k1 - 1, window > 0 ? kj + window - 1 : (1 << 30)) - qt0;
-#pragma unroll
+#pragma unroll RHO_UNROLL
     for (int rho = 0; rho < BQ / 32; ++rho) {
       // rows of s: query 32*rho + 8b + 4h + i of the tile; column: key kj.
       // dP starts from -D of its rows, so the MFMA leaves dP - D.

@@ -25,13 +25,13 @@ constexpr int kFwdShortSeq = 2048;    // and so do problems whose sequences all 
 constexpr int kFwdBQF32 = 128;
 constexpr int kFwdThreadsF32 = 256;
 constexpr int kFwdBK = 64;
-//   backward: both passes run waves of 32 rows (keys for dK/dV, queries for
-//   dQ) and step over 64 partner rows at a time.  Eight waves per item (each
-//   staged partner tile serves 256 rows; four measured 11-12% slower at
-//   d = 128), except with both widths 64: four waves at three per SIMD, so
-//   three independent blocks share a CU and their phases interleave (-3.5%
-//   on the long causal problem, -15% on GPT-2-small sizes).
-constexpr int bwd_waves(int d, int dv) { return d == 64 && dv == 64 ? 4 : 8; }
+//   backward: both passes run four waves of 32 rows (keys for dK/dV, queries
+//   for dQ) per item and step over 64 partner rows at a time.  Several
+//   independent blocks then share a CU (three at d = 64, two at d = 128) and
+//   their phases interleave, which beat eight-wave items that stage each
+//   partner tile once for 256 rows (-4% on the long causal problem, -18% at
+//   GPT-2-small sizes, -10% on the paired window-128 problem).
+constexpr int bwd_waves(int, int) { return 4; }
 constexpr int kBwdBQ = 64;
 //   rotary: threads per block, and the fine step of the two-level cos/sin
 //   table (positions p = hi * kRopeFine + lo).
