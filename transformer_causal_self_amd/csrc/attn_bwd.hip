@@ -99,6 +99,18 @@ constexpr int bwd_waves_per_simd() {
   return D == 64 && DV == 64 ? 3 : 2;
 }
 
+// The lane index as the DMA offsets are formed from it.  Unless both widths
+// are 64 it is hidden from loop-invariant code motion, so the offsets are
+// recomputed per tile rather than held across the loop: there the registers
+// are short, a held offset is spilled, and reloading it before a DMA waits
+// for every load issued before (2-4% at d = 128; at d = 64 the recomputation
+// costs more VALU time than the reloads).
+template <int D, int DV>
+__device__ __forceinline__ int offset_lane(int lane) {
+  if constexpr (!(D == 64 && DV == 64)) asm volatile("" : "+v"(lane));
+  return lane;
+}
+
 // With both widths 64, a wave raises its issue priority while it issues the
 // S and dP MFMAs, so that the matrix unit is fed while the other wave of the
 // SIMD computes its exponentials (-2.5% backward time at d = 64; at d = 128,
@@ -190,12 +202,13 @@ __device__ __forceinline__ void dkv_item(
     const auto rq = make_rsrc(Q + ho + (int64_t)q0 * rs, n * rsb);
     const auto rg = make_rsrc(dO + hoo + (int64_t)q0 * rso, n * rsbo);
     constexpr int NQ = DmaTile<D>::NI, NG = DmaTile<DV>::NI;
+    const int ln = offset_lane<D, DV>(lane);
 #pragma unroll
     for (int j0 = 0; j0 < NQ + NG; j0 += NW) {
       const int j = j0 + w;
-      if (j < NQ) dma16(rq, &bf.q[512 * j], DmaTile<D>::offset(j, lane, rsb));
+      if (j < NQ) dma16(rq, &bf.q[512 * j], DmaTile<D>::offset(j, ln, rsb));
       else if (j < NQ + NG)
-        dma16(rg, &bf.g[512 * (j - NQ)], DmaTile<DV>::offset(j - NQ, lane, rsbo));
+        dma16(rg, &bf.g[512 * (j - NQ)], DmaTile<DV>::offset(j - NQ, ln, rsbo));
     }
     if (tid < 2 * BQ) {
       const int row = q0 + (tid % BQ);
@@ -387,12 +400,13 @@ __device__ __forceinline__ void dq_item(
     const auto rk = make_rsrc(K + hk + (int64_t)k0 * rsk, n * rsbk);
     const auto rv = make_rsrc(V + hv + (int64_t)k0 * rsv, n * rsbv);
     constexpr int NK = DmaTile<D>::NI, NV = DmaTile<DV>::NI;
+    const int ln = offset_lane<D, DV>(lane);
 #pragma unroll
     for (int j0 = 0; j0 < NK + NV; j0 += NW) {
       const int j = j0 + w;
-      if (j < NK) dma16(rk, &bf.k[512 * j], DmaTile<D>::offset(j, lane, rsbk));
+      if (j < NK) dma16(rk, &bf.k[512 * j], DmaTile<D>::offset(j, ln, rsbk));
       else if (j < NK + NV)
-        dma16(rv, &bf.v[512 * (j - NK)], DmaTile<DV>::offset(j - NK, lane, rsbv));
+        dma16(rv, &bf.v[512 * (j - NK)], DmaTile<DV>::offset(j - NK, ln, rsbv));
     }
   };
   issue(sm.b[0], it.k0);
