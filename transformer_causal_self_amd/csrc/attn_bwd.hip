@@ -203,12 +203,26 @@ __device__ __forceinline__ void dkv_item(
     const auto rg = make_rsrc(dO + hoo + (int64_t)q0 * rso, n * rsbo);
     constexpr int NQ = DmaTile<D>::NI, NG = DmaTile<DV>::NI;
     const int ln = offset_lane<D, DV>(lane);
+    if constexpr (D == DV) {
+      // equal widths: Q and dO rows have the same stride (heads x width), so
+      // chunk column j of both tiles uses one offset
 #pragma unroll
-    for (int j0 = 0; j0 < NQ + NG; j0 += NW) {
-      const int j = j0 + w;
-      if (j < NQ) dma16(rq, &bf.q[512 * j], DmaTile<D>::offset(j, ln, rsb));
-      else if (j < NQ + NG)
-        dma16(rg, &bf.g[512 * (j - NQ)], DmaTile<DV>::offset(j - NQ, ln, rsbo));
+      for (int j0 = 0; j0 < NQ; j0 += NW) {
+        const int j = j0 + w;
+        if (j < NQ) {
+          const uint32_t off = DmaTile<D>::offset(j, ln, rsb);
+          dma16(rq, &bf.q[512 * j], off);
+          dma16(rg, &bf.g[512 * j], off);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j0 = 0; j0 < NQ + NG; j0 += NW) {
+        const int j = j0 + w;
+        if (j < NQ) dma16(rq, &bf.q[512 * j], DmaTile<D>::offset(j, ln, rsb));
+        else if (j < NQ + NG)
+          dma16(rg, &bf.g[512 * (j - NQ)], DmaTile<DV>::offset(j - NQ, ln, rsbo));
+      }
     }
     if (tid < 2 * BQ) {
       const int row = q0 + (tid % BQ);
@@ -401,12 +415,24 @@ __device__ __forceinline__ void dq_item(
     const auto rv = make_rsrc(V + hv + (int64_t)k0 * rsv, n * rsbv);
     constexpr int NK = DmaTile<D>::NI, NV = DmaTile<DV>::NI;
     const int ln = offset_lane<D, DV>(lane);
+    if constexpr (D == DV) {
 #pragma unroll
-    for (int j0 = 0; j0 < NK + NV; j0 += NW) {
-      const int j = j0 + w;
-      if (j < NK) dma16(rk, &bf.k[512 * j], DmaTile<D>::offset(j, ln, rsbk));
-      else if (j < NK + NV)
-        dma16(rv, &bf.v[512 * (j - NK)], DmaTile<DV>::offset(j - NK, ln, rsbv));
+      for (int j0 = 0; j0 < NK; j0 += NW) {
+        const int j = j0 + w;
+        if (j < NK) {  // K and V rows: the same stride at equal widths
+          const uint32_t off = DmaTile<D>::offset(j, ln, rsbk);
+          dma16(rk, &bf.k[512 * j], off);
+          dma16(rv, &bf.v[512 * j], off);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j0 = 0; j0 < NK + NV; j0 += NW) {
+        const int j = j0 + w;
+        if (j < NK) dma16(rk, &bf.k[512 * j], DmaTile<D>::offset(j, ln, rsbk));
+        else if (j < NK + NV)
+          dma16(rv, &bf.v[512 * (j - NK)], DmaTile<DV>::offset(j - NK, ln, rsbv));
+      }
     }
   };
   issue(sm.b[0], it.k0);
