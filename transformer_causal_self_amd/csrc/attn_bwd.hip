@@ -99,15 +99,15 @@ constexpr int bwd_waves_per_simd() {
   return D == 64 && DV == 64 ? 3 : 2;
 }
 
-// The lane index as the DMA offsets are formed from it.  Unless both widths
-// are 64 it is hidden from loop-invariant code motion, so the offsets are
-// recomputed per tile rather than held across the loop: there the registers
-// are short, a held offset is spilled, and reloading it before a DMA waits
-// for every load issued before (2-4% at d = 128; at d = 64 the recomputation
-// costs more VALU time than the reloads).
+// The lane index as the DMA offsets are formed from it.  With both widths 128
+// it is hidden from loop-invariant code motion, so the offsets are recomputed
+// per tile rather than held across the loop: there the registers are short,
+// a held offset is spilled, and reloading it before a DMA waits for every
+// load issued before (2-4% faster).  With a width of 64 the recomputation
+// costs more VALU time than it saves (2% at 64/64, 6% with mixed widths).
 template <int D, int DV>
 __device__ __forceinline__ int offset_lane(int lane) {
-  if constexpr (!(D == 64 && DV == 64)) asm volatile("" : "+v"(lane));
+  if constexpr (D == 128 && DV == 128) asm volatile("" : "+v"(lane));
   return lane;
 }
 
@@ -161,10 +161,11 @@ __device__ __forceinline__ void dkv_item(
   const int kj = wk0 + l32;  // this lane's key (column of S)
   const bool kok = kj < it.q1;
   const int trl_q = tr_lane(h, l32, RS), trl_g = tr_lane(h, l32, RSV);
-  // with a width of 128 the two 32-query halves of a tile run one after the
+  // with both widths 128 the two 32-query halves of a tile run one after the
   // other (no overlap): the registers hold only one half's S and dP next to
-  // the dK/dV accumulators (fewer spills, 2-10% faster)
-  constexpr int RHO_UNROLL = D == 64 && DV == 64 ? 2 : 1;
+  // the dK/dV accumulators (fewer spills, 2-10% faster; with mixed widths the
+  // overlap wins by 2%)
+  constexpr int RHO_UNROLL = D == 128 && DV == 128 ? 1 : 2;
 
   bf16x8 kf[D / 16], vf[DV / 16];
 #pragma unroll
