@@ -64,6 +64,9 @@ EDGE = [
     ("window 1", 2, 64, [0, 300], 0, 1, 1),
     ("window 129", 2, 64, [0, 40, 500], 0, 129, 1),
     ("paired H6 window 129", 6, 64, [0, 97, 301], 1, 129, 2),
+    # 128-row items at d = 128 (its own schedule): lengths 127, 128, 129, 257
+    ("item-edge lengths d128", 2, 128, [0, 127, 255, 384, 641], 0, 0, 1),
+    ("window 200 d128", 2, 128, [0, 700], 0, 200, 2),
 ]
 
 
