@@ -14,7 +14,8 @@ import torch
 import oracle
 import transformer_causal_self_amd as tca
 from transformer_causal_self_amd import workloads as wl
-from parity import assert_close, f64, make_plan, oracle_rotated, say, slot_to_token, tol
+from parity import (assert_close, f64, make_plan, oracle_rotated, sample_rows, say,
+                    slot_to_token, tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -106,6 +107,29 @@ def test_bwd_full_size_sampled():
     assert_close(np.stack([dq[s, j] for j, s in q_rows]), sq, tol(w), "dQ rows")
     assert_close(np.stack([dk[s, j] for j, s in k_cols]), sk, tol(w), "dK cols")
     assert_close(np.stack([dv[s, j] for j, s in k_cols]), sv, tol(w), "dV cols")
+
+
+@pytest.mark.parametrize("num", [3, 4])
+def test_bwd_full_size_sampled_windowed(num):
+    """Problems 3 (paired, window 128) and 4 (varlen, window 2048) at full
+    size, d = 128 (the backward's own d = 128 schedule): sampled dQ rows and
+    dK/dV columns from the oracle, sequence edges and tile edges included."""
+    w = dataclasses.replace(W[num], backward=True)
+    inp = wl.generate(w, with_grad=True)
+    say(f"bwd full problem {num}: N={w.n_tokens}")
+    _, _, qt, kt = oracle_rotated(w, inp)
+    dq, dk, dv = gpu_fwd_bwd(w, inp, qt, kt)
+    for x in (dq, dk, dv):
+        assert np.isfinite(x).all()
+    q_rows = sample_rows(w, inp["cu"], np.random.default_rng(10 + num), n_random=24)
+    k_cols = sample_rows(w, inp["cu"], np.random.default_rng(20 + num), n_random=16)
+    sq, sk, sv = oracle.attn_bwd_sampled(f64(qt), f64(kt), f64(inp["v"]), f64(inp["do"]),
+                                         inp["cu"], q_rows, k_cols, w.paired, w.causal,
+                                         w.window, w.scale)
+    at = lambda x, rows: np.stack([x[slot_to_token(s, j, w.heads, w.paired)] for j, s in rows])
+    assert_close(at(dq, q_rows), sq, tol(w), "dQ rows")
+    assert_close(at(dk, k_cols), sk, tol(w), "dK cols")
+    assert_close(at(dv, k_cols), sv, tol(w), "dV cols")
 
 
 def test_bwd_deterministic():
