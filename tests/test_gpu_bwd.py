@@ -14,7 +14,7 @@ import torch
 import oracle
 import transformer_causal_self_amd as tca
 from transformer_causal_self_amd import workloads as wl
-from parity import (assert_close, f64, make_plan, oracle_rotated, sample_rows, say,
+from parity import (LSE_TOL, assert_close, f64, make_plan, oracle_rotated, sample_rows, say,
                     slot_to_token, tol)
 
 pytestmark = pytest.mark.gpu
@@ -130,6 +130,34 @@ def test_bwd_full_size_sampled_windowed(num):
     assert_close(at(dq, q_rows), sq, tol(w), "dQ rows")
     assert_close(at(dk, k_cols), sk, tol(w), "dK cols")
     assert_close(at(dv, k_cols), sv, tol(w), "dV cols")
+
+
+def test_max_heads_fwd_bwd():
+    """num_heads x head_dim at the plan's limit (2^20: 8192 heads of width
+    128), the longest rows the 32-bit tile offsets cover: sampled O, LSE and
+    dQ rows and dK, dV columns for heads at both ends of the row."""
+    w = dataclasses.replace(W[4], n_tokens=200, heads=8192, window=0, doc_range=None, batch=1,
+                            backward=True)
+    inp = wl.tensors(w, seed=31, with_grad=True)
+    inp["cu"] = np.array([0, 200], np.int32)
+    say("fwd+bwd at 8192 heads x 128")
+    _, _, qt, kt = oracle_rotated(w, inp)
+    plan = make_plan(w, inp["cu"])
+    q, k, v, do = qt.cuda(), kt.cuda(), inp["v"].cuda(), inp["do"].cuda()
+    o, lse = tca.attn_fwd(plan, q, k, v)
+    dq, dk, dv = tca.attn_bwd(plan, q, k, v, o, lse, do)
+    torch.cuda.synchronize()
+    rows = [(j, s) for j in (0, 1, 4095, 8191) for s in (0, 1, 63, 64, 127, 128, 199)]
+    o_ref, lse_ref = oracle.attn_fwd_rows(f64(qt), f64(kt), f64(inp["v"]), inp["cu"], rows, 0, 1, 0,
+                                          w.scale)
+    sq, sk, sv = oracle.attn_bwd_sampled(f64(qt), f64(kt), f64(inp["v"]), f64(inp["do"]),
+                                         inp["cu"], rows, rows, 0, 1, 0, w.scale)
+    pick = lambda x: np.stack([x[s, j].cpu().double().numpy() for j, s in rows])
+    assert_close(pick(o), o_ref, tol(w), "O rows")
+    assert_close(np.array([lse[j, s].item() for j, s in rows]), lse_ref, LSE_TOL, "LSE rows")
+    assert_close(pick(dq), sq, tol(w), "dQ rows")
+    assert_close(pick(dk), sk, tol(w), "dK cols")
+    assert_close(pick(dv), sv, tol(w), "dV cols")
 
 
 def test_bwd_deterministic():
