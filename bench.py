@@ -23,6 +23,7 @@ workload on the host cores.
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -65,15 +66,28 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_sources_digest():
-    """Digest of the HIP sources, to tie stored counter readings to a kernel version."""
+def code_text(src):
+    """A source file's code without comments, trailing blanks or empty lines:
+    what the compiler sees, so that editing a comment does not change it."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in src.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
+def kernel_sources_digest(files=None):
+    """Digest of the HIP sources' code (comments ignored), to tie stored
+    counter readings to a kernel version.  `files` maps name -> text (default:
+    the sources in the package's csrc directory)."""
+    if files is None:
+        csrc = os.path.join(ROOT, "transformer_causal_self_amd", "csrc")
+        files = {}
+        for name in sorted(os.listdir(csrc)):
+            if name.endswith((".hip", ".h", ".cpp")):   # build by-products are not sources
+                with open(os.path.join(csrc, name)) as f:
+                    files[name] = f.read()
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "transformer_causal_self_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if not name.endswith((".hip", ".h", ".cpp")):
-            continue            # build by-products are not sources
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+    for name in sorted(files):
+        h.update(name.encode() + code_text(files[name]).encode())
     return h.hexdigest()[:16]
 
 

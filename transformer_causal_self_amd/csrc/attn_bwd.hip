@@ -18,12 +18,11 @@
 //      tail leaves idle):
 //      dK/dV:  one block per 128-key tile of one attention head (four
 //              waves, 32 keys each), looping over the 64-query tiles that
-//              can see it.  S is
-//              formed as Q K^T so that every accumulator lane belongs to one
-//              key; P^T and dS^T then feed the MFMA A operand straight from
-//              registers, and the Q and dO B operands are read transposed
-//              (ds_read_b64_tr_b16) from the same row-major tiles that serve
-//              S and dP.
+//              can see it.  S is formed as Q K^T so that every accumulator
+//              lane belongs to one key; P^T and dS^T then feed the MFMA A
+//              operand straight from registers, and the Q and dO B operands
+//              are read transposed (ds_read_b64_tr_b16) from the same
+//              row-major tiles that serve S and dP.
 //      dQ:     one block per 128-query tile, looping over key tiles;
 //              S^T = K Q^T as in the forward, and K^T for dQ^T = K^T dS^T
 //              read transposed from the row-major K tile.
@@ -112,9 +111,9 @@ __device__ __forceinline__ int offset_lane(int lane) {
 }
 
 // With both widths 64, a wave raises its issue priority while it issues the
-// S and dP MFMAs, so that the matrix unit is fed while the other wave of the
-// SIMD computes its exponentials (-2.5% backward time at d = 64; at d = 128,
-// where the dK/dV registers are already short, it costs 10-13%).
+// S and dP MFMAs, so that the matrix unit is fed while the other waves of the
+// SIMD compute their exponentials (-2.8% backward time at d = 64; with a
+// width of 128, where the registers are already short, it costs 2-8%).
 template <int D, int DV, int LEVEL>
 __device__ __forceinline__ void mfma_priority() {
   if constexpr (D == 64 && DV == 64) __builtin_amdgcn_s_setprio(LEVEL);
