@@ -231,3 +231,22 @@ def test_fwd_rejects_unbound_and_misaligned():
     q = inp["q"].cuda()
     assert lib.attn_fwd(plan.handle, q.data_ptr() + 2, q.data_ptr(), q.data_ptr(),
                         q.data_ptr(), q.data_ptr(), None) == -3
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_empty_problem_every_entry_point(d):
+    """No tokens at all: a valid plan whose launches enqueue nothing and return
+    OK, with zero-size (possibly NULL) buffers, for every entry point."""
+    say(f"empty problem d{d}")
+    plan = tca.attn_plan_create(0, 4, d, "bf16", [0, 0], causal=1, rope="half").bind("cuda")
+    e = lambda *shape, dt=torch.bfloat16: torch.empty(shape, dtype=dt, device="cuda")
+    q, k, v = e(0, 4, d), e(0, 4, d), e(0, 4, d)
+    q2, k2, v2 = tca.rope_qkv(plan, q, k, v, v_out=e(0, 4, d))
+    o, lse = tca.attn_fwd(plan, q2, k2, v2)
+    dq, dk, dv = tca.attn_bwd(plan, q2, k2, v2, o, lse, e(0, 4, d))
+    gq, gk = tca.rope_qkv_bwd(plan, dq, dk)[:2]
+    torch.cuda.synchronize()
+    for x in (q2, k2, v2, o, dq, dk, dv, gq, gk):
+        assert x.shape[0] == 0
+    assert lse.numel() == 0
+
