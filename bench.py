@@ -172,7 +172,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path is single-GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
+              "(the path runs on one GPU; across GPUs it would shard by attention head and by "
+              "sequence, with no exchange)", file=sys.stderr)
         sys.exit(2)
 
     import torch
