@@ -2,22 +2,29 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--paired P]
                     [--kv-heads G] [--v-dim DV] [--qk-norm] [--rope-bwd] [--fp8-inputs]
-                    [--no-cpu-baseline]
+                    [--no-rows] [--no-cpu-baseline]
 
 One step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: rope_qkv (Q, K rotated), attn_fwd (O, LSE) and, for
 the long-context problem, attn_bwd (dQ, dK, dV).  The plan (work lists and
 rotary table) is built once per batch layout, before the timed region.
 
-Printed: ONE JSON line.  `value` is causal TFLOP/s over the step: the exact
-visible-pair FLOPs of the forward (2 (d + dv) per pair; 4 d when dv = d) plus
-the backward (2 (3 d + 2 dv) per pair), divided by the wall time of the step.
-Per-kernel figures come from HIP events recorded on the launch stream around
-every launch of the timed steps.  Each kernel is held to the roofline that
-binds it: rotary passes to HBM bandwidth, attention to the bf16 (or fp32)
-MFMA peak when its FLOPs per algorithmic byte exceed the ridge point, else
-to HBM bandwidth (short windows).  `roofline` is for the kernel that takes
-the most time; every kernel's own roofline is under `kernels`.
+Printed: ONE JSON line.  `value` is the metric's quantity: attention-forward
+TFLOP/s on causal FLOPs (the exact visible-pair FLOPs of attn_fwd, 2 (d + dv)
+per pair, 4 d when dv = d, over the mean attn_fwd kernel time of the timed
+steps).  `step_tflops` is the whole step's rate: forward plus backward FLOPs
+(2 (3 d + 2 dv) per pair) over the step's wall time.  Per-kernel figures
+(mean, median and min) come from HIP events recorded on the launch stream
+around every launch of the timed steps.  Each kernel is held to the roofline
+that binds it: rotary passes to HBM bandwidth, attention to the bf16 (or
+fp32) MFMA peak when its FLOPs per algorithmic byte exceed the ridge point,
+else to HBM bandwidth (short windows).  `roofline` is for the kernel that
+takes the most time; every kernel's own roofline is under `kernels`.
+`rows` (default run only) times rope_qkv and attn_fwd of the two varlen
+problems (65536 tokens, 6 heads, d = 128: paired window 128, and window 2048)
+with three input/output sets used in turn, so that each launch finds its data
+outside the 256 MiB last-level cache.  `copy_gbs` is a plain 1 GiB device
+copy (read + write bytes over its time), the practical HBM ceiling.
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same
 workload on the host cores.
 """
@@ -45,6 +52,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the rope_qkv / attn_fwd rows of the two varlen problems")
     ap.add_argument("--cpu-seconds", type=float, default=30.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--paired", type=int, choices=(0, 1, 2), default=None,
@@ -106,6 +115,107 @@ def stored_traffic(kernel, workload, digest):
     return r.get("bytes_per_launch")
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def stats_ms(pairs):
+    """mean, median and min of the elapsed times (ms) of (start, end) event pairs."""
+    import numpy as np
+    t = np.array([a.elapsed_time(b) for a, b in pairs])
+    return float(t.mean()), float(np.median(t)), float(t.min())
+
+
+def copy_gbs(dev, reps=5):
+    """Read + write GB/s of a plain 1 GiB device-to-device copy (median of reps)."""
+    import numpy as np
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ev = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    del src, dst
+    return 2.0 * (1 << 30) / (ms * 1e-3) / 1e9
+
+
+def varlen_rows(dev, reps=10, sets=3):
+    """rope_qkv and attn_fwd of the two varlen problems, each launch on one of
+    `sets` copies of its inputs and outputs in turn (the launch's data was last
+    touched `sets - 1` launches earlier: beyond the last-level cache)."""
+    import torch
+    import transformer_causal_self_amd as tca
+    from transformer_causal_self_amd import workloads as wl
+    out = {}
+    for num in (3, 4):
+        w = wl.WORKLOADS[num]
+        inp = wl.generate(w)
+        plan = tca.attn_plan_create(w.n_tokens, w.heads, w.head_dim, "bf16", inp["cu"],
+                                    causal=w.causal, window=w.window, softmax_scale=w.scale,
+                                    rope=w.rope, rope_base=w.rope_base,
+                                    paired=w.paired).bind(dev)
+        info = plan.info
+        base = {n: inp[n].to(dev) for n in ("q", "k", "v")}
+        bufs = []
+        for i in range(sets):
+            q, k, v = (base[n] if i == 0 else base[n].clone() for n in ("q", "k", "v"))
+            bufs.append(dict(q=q, k=k, v=v, q2=torch.empty_like(q), k2=torch.empty_like(k),
+                             o=torch.empty_like(q),
+                             lse=torch.empty((info["attn_heads"], info["slots"]),
+                                             dtype=torch.float32, device=dev)))
+        ev = {"rope_qkv": [], "attn_fwd": []}
+        for r in range(2 + reps):
+            b = bufs[r % sets]
+            for name, fn in (("rope_qkv", lambda: tca.rope_qkv(plan, b["q"], b["k"],
+                                                              q_out=b["q2"], k_out=b["k2"])),
+                             ("attn_fwd", lambda: tca.attn_fwd(plan, b["q2"], b["k2"], b["v"],
+                                                              b["o"], b["lse"]))):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                if r >= 2:
+                    ev[name].append((e0, e1))
+        torch.cuda.synchronize()
+        row = {"workload": w.name, "sets": sets, "reps": reps}
+        for name in ev:
+            mean, med, mn = stats_ms(ev[name])
+            if name == "rope_qkv":
+                by = info["rope_bytes"]
+                row[name] = {"bound": "hbm", "gbs_median": by / (med * 1e-3) / 1e9,
+                             "gbs_best": by / (mn * 1e-3) / 1e9,
+                             "frac": by / (med * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                             "ms_mean": mean, "ms_median": med, "ms_min": mn}
+            else:
+                fl, by = info["fwd_flops"], info["fwd_bytes"]
+                if fl / by >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+                    row[name] = {"bound": "mfma", "tflops_median": fl / (med * 1e-3) / 1e12,
+                                 "frac": fl / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+                else:
+                    row[name] = {"bound": "hbm", "gbs_median": by / (med * 1e-3) / 1e9,
+                                 "frac": by / (med * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                 "tflops_median": fl / (med * 1e-3) / 1e12}
+                row[name].update(ms_mean=mean, ms_median=med, ms_min=mn)
+        out[f"problem{num}"] = row
+        del bufs, base, plan
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, inp, seconds, norm=False, fp8=None):
     """fp64 oracle on a bounded random sample of the forward's query rows (plus
     its RoPE of every token), scaled to causal TFLOP/s."""
@@ -119,6 +229,8 @@ def cpu_baseline(w, inp, seconds, norm=False, fp8=None):
 
     def visible(s):
         k = np.searchsorted(bounds, s, side="right") - 1
+        if not w.causal:
+            return bounds[k + 1] - bounds[k]
         n = s - bounds[k] + 1
         return min(n, w.window) if w.window > 0 else n
 
@@ -163,7 +275,7 @@ def cpu_baseline(w, inp, seconds, norm=False, fp8=None):
     flops = sum(2.0 * (w.head_dim + (w.v_dim or w.head_dim)) * visible(int(s))
                 for s in rows[:, 1])
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{n} random (head, query) rows of this workload's forward (causal FLOPs "
                       f"{flops / 1e9:.1f} GFLOP) plus the RoPE of every token, fp64, {dt:.1f} s"}
 
@@ -279,7 +391,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    kern_ms = {n: sum(a.elapsed_time(b) for a, b in events[n]) / len(events[n]) for n in names}
+    kern_stats = {n: stats_ms(events[n]) for n in names}
+    kern_ms = {n: kern_stats[n][0] for n in names}
     digest = kernel_sources_digest()
     wname = f"problem{w.num}" + ("" if args.paired is None else f"-paired{w.paired}") + (
         "" if args.kv_heads is None else f"-kv{w.kv_heads}") + (
@@ -322,14 +435,15 @@ def main():
                       "frac": ach / PEAK_HBM_GBS, "tflops": fl / t / 1e12}
         rl["traffic"] = stored_traffic(n, wname, digest)
         rl["ms"] = kern_ms[n]
+        rl["ms_median"], rl["ms_min"] = kern_stats[n][1], kern_stats[n][2]
         kernels[n] = rl
     dominant = max(names, key=lambda n: kern_ms[n])
-    roof = {k2_: v_ for k2_, v_ in kernels[dominant].items() if k2_ != "ms"}
+    roof = {k2_: v_ for k2_, v_ in kernels[dominant].items() if not k2_.startswith("ms")}
     roof["kernel"] = dominant
 
     out = {
         "metric": METRIC,
-        "value": step_flops / (ms_step * 1e-3) / 1e12,
+        "value": info["fwd_flops"] / (kern_ms["attn_fwd"] * 1e-3) / 1e12,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -351,13 +465,16 @@ def main():
                    "step": "+".join(names), "parallelism": "single GPU"},
         "roofline": roof,
         "kernels": kernels,
-        "fwd_tflops": info["fwd_flops"] / (kern_ms["attn_fwd"] * 1e-3) / 1e12,
         "fwd_frac_bf16_peak": info["fwd_flops"] / (kern_ms["attn_fwd"] * 1e-3) / 1e12 / peak_mm,
+        "step_tflops": step_flops / (ms_step * 1e-3) / 1e12,
         "rope_gbs": kernels["rope_qkv"]["achieved"],
         "step_flops": step_flops,
         "visible_pairs": info["visible_pairs"],
         "kernel_sources": digest,
     }
+    if not args.no_rows and args.workload == 5:
+        out["rows"] = varlen_rows(dev)
+    out["copy_gbs"] = copy_gbs(dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds, args.qk_norm, fp8)
     print(json.dumps(out), flush=True)

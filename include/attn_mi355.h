@@ -63,7 +63,13 @@
  *   - The caller owns every device buffer, the workspace and the stream.  The
  *     plan owns only host memory and is immutable after attn_plan_bind, so
  *     several launches may share it.  Launches that share one bound workspace
- *     may run concurrently except attn_bwd, which writes a scratch area of it.
+ *     may run concurrently, except two attn_fwd or two attn_bwd calls: each
+ *     of those entry points keeps scratch data in the workspace (attn_fwd the
+ *     merge counters and partial results of query tiles whose key range the
+ *     plan cut into parts, attn_bwd the per-row D values).  The merge
+ *     counters start at zero at attn_plan_bind and every attn_fwd leaves them
+ *     at zero; a launch that does not run to completion leaves them
+ *     undefined, and binding again resets them.
  *   - No call throws, aborts or prints.
  */
 #ifndef ATTN_MI355_H
@@ -136,16 +142,27 @@ typedef struct {
                                 sequence, doubled when paired) */
   int32_t kv_heads;          /* K/V heads: Hkv, or H' when not grouped */
   int32_t v_head_dim;        /* dv */
+  int32_t fwd_split_items;   /* forward query tiles whose key range is cut into
+                                parts run by separate workgroups (merged in the
+                                same launch) */
 } attn_plan_info;
 
 /*
+ * The problem statement follows the varlen attention call of "Paired Head
+ * Attention", section "Source 3" (packed tokens, cu_seqlens, causal, a left
+ * window, softmax scale), with the rotary and pairing arguments of its
+ * sections "Zero-copy RoPE" and "Source 4", and the textbook module's
+ * num_kv_heads ("Upgrading a textbook decoder", section 4).
  * Validate a problem and build its host plan: paired slot boundaries
  * (2 * cu when paired), the per-token rotary positions, the fp64-computed
  * cos/sin table rounded to fp32 (two levels: angles lo * theta and
  * 64 hi * theta, combined by angle addition in the kernels for position
  * 64 hi + lo, so the table stays cache resident), and the tile work lists
  * (fully masked causal and window tiles are never listed; longest items
- * first).  Host only: makes
+ * first; a forward query tile whose key range is long next to the mean load
+ * of a workgroup slot may be cut into parts that separate workgroups run and
+ * the last of them merges).  A window of at least the longest sequence's
+ * slot count hides nothing and is treated as no window.  Host only: makes
  * no HIP call.  On success *out owns a plan to free with attn_plan_destroy.
  * Errors: ATTN_E_INVALID (bad field), ATTN_E_UNSUPPORTED (head_dim or
  * v_head_dim not 64 or 128; v_head_dim != head_dim with fp32; grouped K/V
@@ -178,12 +195,17 @@ attn_status attn_plan_stats(const attn_plan *plan, attn_plan_info *info);
  * query slots).  The backward lists are empty for fp32 problems.  The head
  * of every item is a query (attention) head; with grouped K/V heads the key
  * tiles of a group's query heads add into the same dK/dV rows.
- * Each item is 8 int32: {attention head, r0, r1, s0, s1, stream, 0, 0}
- * where stream numbers the (attention head, sequence) pairs.  The list order
- * is the launch order: item i runs as workgroup i, on XCD i mod 8; items of one
+ * Each item is 8 int32: {attention head, r0, r1, s0, s1, x, y, z}.
+ * Backward lists: x = stream, the index of the (attention head, sequence)
+ * pair, y = z = 0.  Forward list: x = merge group (-1 when the query tile is
+ * whole, else the index of the cut query tile), y = the part's
+ * partial-result slot (consecutive for the parts of one group), z = part
+ * index << 16 | number of parts (1 when whole).  The list order is the
+ * launch order: item i runs as workgroup i, on XCD i mod 8; items of one
  * stream and nearby tiles share an XCD (and its L2), longest first within it.
  * Forward and dQ: query slots [r0, r1) of one sequence and the key slots
- * [s0, s1) any of them may see.  Backward: key slots [r0, r1) and the query slots
+ * [s0, s1) any of them may see (for a part of a cut forward tile: its share
+ * of them, the parts tiling the tile's range in part order).  Backward: key slots [r0, r1) and the query slots
  * [s0, s1) that may see them.  Copies min(count, capacity) items into out
  * (out may be NULL when capacity is 0) and stores the total count in *count.
  */
@@ -255,7 +277,12 @@ attn_status attn_fwd(const attn_plan *plan, const void *q, const void *k, const 
 
 /*
  * Backward of attn_fwd with respect to its inputs q, k, v (the rotated
- * values), recomputing P = exp(s q k^T - LSE):
+ * values).  The pages print no correct backward: this is the chain rule
+ * through the forward as defined ("mHC module" article, section 2.1:
+ * softmax of the masked, scaled scores, times V) with the softmax Jacobian
+ * diag(P) - P P^T; the backward printed in that article's section 4.1 is not
+ * the derivative of softmax and is not followed.  Recomputing
+ * P = exp(s q k^T - LSE):
  *     D_i = dO_i . O_i,  dS = P o (dO V^T - D),
  *     dV = P^T dO,  dQ = s dS K,  dK = s dS^T Q.
  * q: dense [N, H, d], k: [N, Hkv, d], v: [N, Hkv, dv], o, d_o: [N, H, dv], in

@@ -28,7 +28,8 @@ def _load():
     if _lib is not None:
         return _lib
     path = _build.LIB
-    if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+    if not os.path.exists(path) or (getattr(_build, "SRC_CHECK", True) and
+                                    os.path.getmtime(path) < os.path.getmtime(_build.SRC)):
         _build.build()
     lib = ctypes.CDLL(path)
     lib.oracle_num_threads.restype = ctypes.c_int

@@ -52,17 +52,45 @@ def oracle_rotated(w, inp):
     return qr, kr, qt, kt
 
 
-def assert_close(got, want, bound, what):
+def error_figures(got, want):
+    """max-abs error; max-rel error over the elements with |want| >= 1e-3 of
+    the largest |want| (smaller ones only measure cancellation); and the
+    largest error of a row (last axis) divided by that row's RMS in the
+    oracle (rows with an RMS below 1e-3 of the largest row RMS skipped)."""
+    err = np.abs(got - want)
+    if not err.size:
+        return 0.0, 0.0, 0.0
+    mag = np.abs(want)
+    big = mag >= 1e-3 * mag.max() if mag.max() > 0 else np.zeros_like(mag, bool)
+    rel = float((err[big] / mag[big]).max()) if big.any() else 0.0
+    if want.ndim >= 2:
+        rms = np.sqrt((want * want).mean(axis=-1))
+        keep = rms >= 1e-3 * rms.max() if rms.max() > 0 else np.zeros_like(rms, bool)
+        row = float((err.max(axis=-1)[keep] / rms[keep]).max()) if keep.any() else 0.0
+    else:
+        row = rel
+    return float(err.max()), rel, row
+
+
+def assert_close(got, want, bound, what, row_bound=None):
+    """Element-by-element comparison against the oracle: the max-abs error must
+    stay within `bound` (and, when given, every row's max error within
+    `row_bound` times that row's RMS).  Prints max-abs, max-rel and the
+    row-relative figure."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     assert got.shape == want.shape, (what, got.shape, want.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite values"
-    err = np.abs(got - want)
-    m = float(err.max()) if err.size else 0.0
+    m, rel, row = error_figures(got, want)
+    say(f"  {what}: max-abs {m:.2e} (bound {bound:.0e}), max-rel {rel:.2e}, "
+        f"max err / row RMS {row:.2e}")
     if m > bound:
+        err = np.abs(got - want)
         idx = np.unravel_index(int(err.argmax()), err.shape)
         raise AssertionError(f"{what}: max-abs error {m:.3e} > {bound:.1e} at {idx} "
                              f"(got {got[idx]:.6f}, want {want[idx]:.6f})")
+    if row_bound is not None and row > row_bound:
+        raise AssertionError(f"{what}: a row's error is {row:.3e} of its RMS > {row_bound:.1e}")
     return m
 
 

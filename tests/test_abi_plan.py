@@ -161,13 +161,69 @@ def test_grouped_kv_work_lists(H, Hkv, window):
         for head, r0, r1, *_ in p.work_items(which):
             seen[head, r0:r1] += 1
         assert (seen == 1).all(), which
-    fwd = p.work_items(0)
+    bwd = p.work_items(1)
     xcds = {}
-    for i, it in enumerate(fwd):
+    for i, it in enumerate(bwd):
         xcds.setdefault((int(it[5]), int(it[1])), set()).add(i % 8)
     # (the tail of the list borrows items across XCDs to balance load)
     assert sum(len(x) == 1 for x in xcds.values()) >= 0.6 * len(xcds)
-    assert {int(it[0]) // (H // Hkv) for it in fwd if it[5] == fwd[0][5]} == {fwd[0][0] // (H // Hkv)}
+    assert {int(it[0]) // (H // Hkv) for it in bwd if it[5] == bwd[0][5]} == {bwd[0][0] // (H // Hkv)}
+
+
+def whole_items(fwd):
+    """The forward list with the parts of every cut query tile joined back:
+    checks that parts of one group share the head and query tile, number
+    0..n-1 once each, hold consecutive partial slots, and tile the key range
+    in part order without gaps or overlaps."""
+    groups = {}
+    whole = []
+    for it in fwd:
+        g, slot, pp = int(it[5]), int(it[6]), int(it[7])
+        part, parts = pp >> 16, pp & 0xFFFF
+        if g < 0:
+            assert parts == 1 and part == 0
+            whole.append(tuple(int(x) for x in it[:5]))
+            continue
+        assert parts >= 2 and 0 <= part < parts
+        groups.setdefault(g, []).append((part, parts, slot, tuple(int(x) for x in it[:5])))
+    slots = set()
+    for g, ps in groups.items():
+        ps.sort()
+        assert [p[0] for p in ps] == list(range(ps[0][1]))
+        assert len({p[1] for p in ps}) == 1
+        first = ps[0][2]
+        assert [p[2] for p in ps] == list(range(first, first + len(ps)))
+        slots.update(p[2] for p in ps)
+        items = [p[3] for p in ps]
+        assert len({it[:3] for it in items}) == 1
+        for a, b in zip(items, items[1:]):
+            assert a[4] == b[3] and (b[3] - items[0][3]) % 64 == 0
+        whole.append(items[0][:4] + (items[-1][4],))
+    assert sorted(groups) == list(range(len(groups)))
+    assert len(slots) == sum(len(ps) for ps in groups.values())
+    return np.array(sorted(whole), dtype=np.int64).reshape(-1, 5)
+
+
+def test_long_causal_forward_is_cut_and_balanced_one_is_not():
+    # the schedule cuts the key range of the longest query tiles of a long
+    # causal sequence into parts (the tail of a longest-first list of whole
+    # tiles is the last query tile alone); a list that already balances stays
+    # whole, and so does every fp32 list (its kernel has no merge)
+    p = plan(num_tokens=16384, cu_seqlens=[0, 16384], num_heads=12)
+    fwd = p.work_items(0)
+    assert p.info["fwd_split_items"] > 0
+    assert p.info["fwd_split_items"] == len({int(g) for g in fwd[:, 5] if g >= 0})
+    whole = whole_items(fwd)
+    assert len(whole) == 12 * 64
+    steps = (fwd[:, 4] - fwd[:, 3] + 63) // 64
+    assert steps.max() < 256
+    # many tiles of similar length over the whole chip: nothing to gain
+    w = wl.WORKLOADS[4]
+    q = plan(num_tokens=w.n_tokens, cu_seqlens=wl.cu_seqlens(w), num_heads=w.heads,
+             head_dim=w.head_dim, window=w.window, rope="adjacent")
+    assert q.info["fwd_split_items"] == 0 and (q.work_items(0)[:, 5] == -1).all()
+    fp = plan(num_tokens=16384, cu_seqlens=[0, 16384], num_heads=12, dtype="fp32")
+    assert fp.info["fwd_split_items"] == 0
 
 
 def dense_pairs(cu, mult, causal, window):
@@ -207,7 +263,7 @@ def test_counts_and_work_lists_cover_the_mask(cu, H, paired, causal, window):
     def seq_of(slot):
         s = np.searchsorted(bounds, slot, side="right") - 1
         return bounds[s], bounds[s + 1]
-    for lst, rows_max in ((fwd, 256), (dq, 128)):
+    for lst, rows_max in ((whole_items(fwd), 256), (dq, 128)):
         seen = np.zeros((Hs, N * mult), dtype=int)
         for head, q0, q1, k0, k1, *_ in lst:
             assert 0 < q1 - q0 <= rows_max
@@ -234,11 +290,12 @@ def test_counts_and_work_lists_cover_the_mask(cu, H, paired, causal, window):
     # roughly longest first
     for lst, step in ((fwd, 64), (bwd, 64), (dq, 64)):
         steps = np.ceil((lst[:, 4] - lst[:, 3]) / step)
-        per_stream = {}
-        for i, it in enumerate(lst):
-            per_stream.setdefault(int(it[5]), set()).add(i % 8)
-        n_streams = len(per_stream)
-        assert n_streams == len({(int(a), int(b)) for a, b in zip(lst[:, 0], lst[:, 5])})
+        if lst is not fwd:      # the backward lists carry the stream
+            per_stream = {}
+            for i, it in enumerate(lst):
+                per_stream.setdefault(int(it[5]), set()).add(i % 8)
+            n_streams = len(per_stream)
+            assert n_streams == len({(int(a), int(b)) for a, b in zip(lst[:, 0], lst[:, 5])})
         for x in range(8):
             sub = steps[x::8]
             if len(sub) > 2:
@@ -274,3 +331,17 @@ def test_varlen_layouts_count_like_the_closed_form(num):
         i = np.arange(L)
         total += int(np.minimum(i + 1, w.window).sum())
     assert p.info["visible_pairs"] == Hs * total
+
+
+@pytest.mark.parametrize("window,same", [(2147483647, True), (1600, True), (1599, False)])
+def test_window_spanning_every_sequence_is_no_window(window, same):
+    # a window at least as long as the longest sequence (here 1600 slots)
+    # hides no key: the plan drops it, so the kernels never add a huge window
+    # to a slot index
+    cu = [0, 700, 2300]
+    a = plan(num_tokens=2300, cu_seqlens=cu, window=window)
+    b = plan(num_tokens=2300, cu_seqlens=cu, window=0)
+    if same:
+        assert all(np.array_equal(a.work_items(i), b.work_items(i)) for i in range(3))
+    assert (a.info["visible_pairs"] == b.info["visible_pairs"]) == same
+    assert a.info["visible_pairs"] == 2 * int(brute.dense_mask(cu, 1, 1, window).sum())

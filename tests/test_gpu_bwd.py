@@ -68,6 +68,8 @@ EDGE = [
     # 128-row items at d = 128 (its own schedule): lengths 127, 128, 129, 257
     ("item-edge lengths d128", 2, 128, [0, 127, 255, 384, 641], 0, 0, 1),
     ("window 200 d128", 2, 128, [0, 700], 0, 200, 2),
+    # a window of INT32_MAX slots (a common "no window" value) is no window
+    ("window INT32_MAX", 2, 64, [0, 90, 400], 0, 2147483647, 1),
 ]
 
 
@@ -86,9 +88,24 @@ def test_bwd_edge_cases(case):
         assert_close(g, r, tol(w), n)
 
 
+def sampled_slots(T, H, rng, n=512):
+    """(head, slot) pairs for a sampled full-size check: in every head the
+    first and last slots, the edges of the 64- and 128-row tiles and of the
+    2048-slot runs that share an XCD, then random slots, half of them among the
+    last 2048 (where a row sees the most keys and its values are smallest)."""
+    fixed = [0, 1, 63, 64, 127, 128, 2047, 2048, T // 2 - 1, T // 2, T - 129, T - 128, T - 2,
+             T - 1]
+    out = {(h, s) for h in range(H) for s in fixed if 0 <= s < T}
+    while len(out) < n:
+        s = int(rng.integers(0, T)) if len(out) % 2 else int(rng.integers(max(0, T - 2048), T))
+        out.add((int(rng.integers(H)), s))
+    return sorted(out)
+
+
 def test_bwd_full_size_sampled():
     """The full long-context problem (T=16384, H=12, d=64); the oracle computes
-    sampled dQ rows and dK/dV columns."""
+    512 sampled dQ rows and 512 dK/dV columns (every head's tile edges and
+    ends, random slots weighted toward the late ones)."""
     w = W[5]
     inp = wl.generate(w)
     say("bwd full long-context problem")
@@ -96,12 +113,9 @@ def test_bwd_full_size_sampled():
     dq, dk, dv = gpu_fwd_bwd(w, inp, qt, kt)
     for x in (dq, dk, dv):
         assert np.isfinite(x).all()
-    rng = np.random.default_rng(5)
-    T, Hs = w.n_tokens, w.heads
-    q_rows = [(int(rng.integers(Hs)), int(s)) for s in
-              list(rng.integers(0, T, 24)) + [0, 1, 127, 128, T - 1]]
-    k_cols = [(int(rng.integers(Hs)), int(s)) for s in
-              list(rng.integers(0, T, 16)) + [0, 1, 63, 64, T - 1]]
+    q_rows = sampled_slots(w.n_tokens, w.heads, np.random.default_rng(5))
+    k_cols = sampled_slots(w.n_tokens, w.heads, np.random.default_rng(6))
+    assert len(q_rows) >= 512 and len(k_cols) >= 512
     sq, sk, sv = oracle.attn_bwd_sampled(f64(qt), f64(kt), f64(inp["v"]), f64(inp["do"]),
                                          inp["cu"], q_rows, k_cols, 0, 1, 0, 0.0)
     assert_close(np.stack([dq[s, j] for j, s in q_rows]), sq, tol(w), "dQ rows")
@@ -180,3 +194,29 @@ def test_bwd_fp32_is_unsupported():
         tca.attn_bwd(plan, q, q, q, q, lse, q,
                      *(torch.empty(q.shape, device="cuda") for _ in range(3)))
     assert e.value.status == -2
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_non_causal_varlen(d):
+    """causal = 0: every key of a query's sequence is visible (ragged lengths,
+    an empty and a one-token sequence), forward and backward against the
+    oracle."""
+    cu = [0, 90, 90, 91, 300, 557]
+    w = dataclasses.replace(W[5], n_tokens=cu[-1], heads=2, head_dim=d, causal=0, window=0,
+                            rope=1, doc_range=None, batch=1)
+    inp = wl.tensors(w, seed=41, with_grad=True)
+    inp["cu"] = np.array(cu, np.int32)
+    say(f"non-causal varlen fwd+bwd d{d}")
+    _, _, qt, kt = oracle_rotated(w, inp)
+    plan = make_plan(w, inp["cu"])
+    q, k, v, do = qt.cuda(), kt.cuda(), inp["v"].cuda(), inp["do"].cuda()
+    o, lse = tca.attn_fwd(plan, q, k, v)
+    dq, dk, dv = tca.attn_bwd(plan, q, k, v, o, lse, do)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_fwd(f64(qt), f64(kt), f64(inp["v"]), inp["cu"], 0, 0, 0,
+                                     w.scale)
+    assert_close(o.cpu().double().numpy(), o_ref, tol(w), "O")
+    assert_close(lse.cpu().double().numpy(), lse_ref, LSE_TOL, "LSE")
+    ref = oracle_bwd(w, inp, qt, kt)
+    for g, r, n in zip((dq, dk, dv), ref, ("dQ", "dK", "dV")):
+        assert_close(g.cpu().double().numpy(), r, tol(w), n)

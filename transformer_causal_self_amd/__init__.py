@@ -59,7 +59,7 @@ class _Info(ctypes.Structure):
                 ("fwd_items", ctypes.c_int64), ("bwd_items", ctypes.c_int64),
                 ("slots", ctypes.c_int64), ("attn_heads", ctypes.c_int32),
                 ("max_positions", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
-                ("v_head_dim", ctypes.c_int32)]
+                ("v_head_dim", ctypes.c_int32), ("fwd_split_items", ctypes.c_int32)]
 
 
 _lib = None

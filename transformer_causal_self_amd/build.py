@@ -21,9 +21,17 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer (the sanitized CPU
+# test run, tests/sanitize.py): every flag applies to the host pass only.
+SAN_FLAGS = []
+for _f in ("-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer", "-g"):
+    SAN_FLAGS += ["-Xarch_host", _f]
+
+
+def _compile(src: str, verbose: bool, build_dir: str, extra) -> str:
+    obj = os.path.join(build_dir, src + ".o")
+    cmd = [HIPCC] + FLAGS + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -37,16 +45,20 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False, out: str = LIB) -> str:
+    """Compile and link the library into `out`.  sanitize=True adds host-side
+    ASan/UBSan (device code unchanged) and uses its own object directory."""
+    build_dir = BUILD + ("_san" if sanitize else "")
+    os.makedirs(build_dir, exist_ok=True)
+    extra = SAN_FLAGS if sanitize else []
     with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra), SOURCES))
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out + ".tmp"] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

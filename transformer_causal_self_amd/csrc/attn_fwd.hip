@@ -392,7 +392,8 @@ template <int D, int DV, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
     const WorkItem *__restrict__ items, const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const __bf16 *__restrict__ V, __bf16 *__restrict__ O, float *__restrict__ LSE, int Hs,
-    int Hks, int G, int64_t Ns, float scale, float scale_log2, int causal, int window) {
+    int Hks, int G, int64_t Ns, float scale, float scale_log2, int causal, int window,
+    int *__restrict__ split_cnt, float *__restrict__ split_part) {
   constexpr bool VT = NW == 8;  // V layout (see SmemBF)
   constexpr int KS = SmemBF<D, DV, VT>::KS, VS = SmemBF<D, DV, VT>::VS;
   __shared__ __attribute__((aligned(16))) SmemBF<D, DV, VT> sm;
@@ -558,6 +559,91 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
     __syncthreads();
   }
 
+  if (it.pad0 >= 0) {
+    // The item's key range was cut into parts run by separate blocks (this
+    // one ran [k0, k1)).  Each part leaves its unnormalised O^T, reference max
+    // and sum in its partial slot, then counts itself in; the last to arrive
+    // merges all parts: with M = max_p m_p and c_p = 2^((m_p - M) s log2 e),
+    // O^T = sum c_p O^T_p and l = sum c_p l_p -- the rescaling of the online
+    // softmax, once per part.  Nobody waits: blocks that are not last just
+    // finish.  The merge folds the parts in part order whichever block does
+    // it (its own part from registers, the same values it stored), so the
+    // result does not depend on the order in which the parts finished.  The
+    // slots are written and read with device-coherent accesses, so no
+    // cache-wide write-back or invalidation is needed around the count.
+    const int part = it.pad2 >> 16, parts = it.pad2 & 0xffff;
+    constexpr int CH = fwd_partial_chunks(DV);
+    constexpr uint32_t kWaveBytes = CH * 64 * 16;  // one wave's share of a slot
+    // this wave's region of part pp's slot
+    const auto region = [&](int pp) {
+      const char *base = reinterpret_cast<const char *>(split_part) +
+                         ((int64_t)(it.pad1 - part + pp) * NW + w) * kWaveBytes;
+      return make_rsrc(base, kWaveBytes);
+    };
+    const uint32_t lo = 16u * lane;
+    {
+      const auto mine = region(part);
+#pragma unroll
+      for (int dl = 0; dl < DV / 32; ++dl)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          store16_coherent(mine, lo + 1024u * (4 * dl + b),
+                           floatx4{o[dl][4 * b], o[dl][4 * b + 1], o[dl][4 * b + 2],
+                                   o[dl][4 * b + 3]});
+      store16_coherent(mine, lo + 1024u * (CH - 1), floatx4{m, l, 0.0f, 0.0f});
+    }
+    // The slot is complete and visible device-wide once the stores have
+    // drained; only then does the block count itself in.
+    wait_stores();
+    __shared__ int last;
+    __syncthreads();
+    if (tid == 0)
+      last = __hip_atomic_fetch_add(split_cnt + it.pad0, 1, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == parts - 1;
+    __syncthreads();
+    if (!last) return;
+    if (tid == 0)  // every part has counted: ready for the next launch
+      __hip_atomic_store(split_cnt + it.pad0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    floatx16 acc[DV / 32];
+#pragma unroll
+    for (int dl = 0; dl < DV / 32; ++dl) acc[dl] = floatx16{};
+    float am = kMinusBig, al = 0.0f;
+    for (int pp = 0; pp < parts; ++pp) {
+      const bool own = pp == part;  // block-uniform
+      const auto src = region(pp);
+      float pm = m, pl = l;
+      if (!own) {
+        const floatx4 ml = load16_coherent(src, lo + 1024u * (CH - 1));
+        pm = ml[0];
+        pl = ml[1];
+      }
+      float ca = 0.0f, cb = 1.0f;  // part 0: acc = its values
+      if (pp > 0) {
+        const float mx = fmaxf(am, pm);
+        ca = fast_exp2((am - mx) * scale_log2);
+        cb = fast_exp2((pm - mx) * scale_log2);
+      }
+      am = pp > 0 ? fmaxf(am, pm) : pm;
+      al = al * ca + pl * cb;
+#pragma unroll
+      for (int dl = 0; dl < DV / 32; ++dl)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          floatx4 x;
+          if (own)
+            x = floatx4{o[dl][4 * b], o[dl][4 * b + 1], o[dl][4 * b + 2], o[dl][4 * b + 3]};
+          else
+            x = load16_coherent(src, lo + 1024u * (4 * dl + b));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[dl][4 * b + i] = acc[dl][4 * b + i] * ca + x[i] * cb;
+        }
+    }
+    m = am;
+    l = al;
+#pragma unroll
+    for (int dl = 0; dl < DV / 32; ++dl) o[dl] = acc[dl];
+  }
+
   // epilogue: O = O^T / l, LSE = s * m + ln l
   const float lt = halves_sum(l);
   if (qok) {
@@ -581,6 +667,8 @@ hipError_t launch_typed(const attn_plan *p, const void *q, const void *k, const 
                         float *lse, hipStream_t stream) {
   static_assert(std::is_same<T, __bf16>::value || DV == D, "fp32 keeps one head width");
   const WorkItem *items = reinterpret_cast<const WorkItem *>(p->ws + p->off_fwd);
+  int *split_cnt = reinterpret_cast<int *>(p->ws + p->off_split_cnt);
+  float *split_part = reinterpret_cast<float *>(p->ws + p->off_split_part);
   const unsigned n = (unsigned)p->fwd.size();
   if (n == 0) return hipSuccess;
   const float scale = p->p.scale;
@@ -590,13 +678,13 @@ hipError_t launch_typed(const attn_plan *p, const void *q, const void *k, const 
     hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, kFwdBQ / 32>), dim3(n), dim3(2 * kFwdBQ), 0, stream,
                        items, static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
                        static_cast<const __bf16 *>(v), static_cast<__bf16 *>(o), lse, P.Hs, P.Hks,
-                       P.G, P.Ns, scale, scale_log2, P.causal, P.window);
+                       P.G, P.Ns, scale, scale_log2, P.causal, P.window, split_cnt, split_part);
   else if (std::is_same<T, __bf16>::value)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, kFwdBQShort / 32>), dim3(n),
                        dim3(2 * kFwdBQShort), 0, stream, items, static_cast<const __bf16 *>(q),
                        static_cast<const __bf16 *>(k), static_cast<const __bf16 *>(v),
                        static_cast<__bf16 *>(o), lse, P.Hs, P.Hks, P.G, P.Ns, scale, scale_log2,
-                       P.causal, P.window);
+                       P.causal, P.window, split_cnt, split_part);
   else
     hipLaunchKernelGGL((fwd_kernel<float, D>), dim3(n), dim3(kFwdThreadsF32), 0, stream, items,
                        static_cast<const float *>(q), static_cast<const float *>(k),

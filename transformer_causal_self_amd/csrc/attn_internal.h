@@ -39,11 +39,35 @@ constexpr int kRopeThreads = 256;
 constexpr int kRopeFine = 64;
 // Work-list chunk: consecutive tiles of one head and sequence kept on one XCD.
 constexpr int kXcdChunk = 16;
+// Compute units of the chip (8 XCDs of 32).
+constexpr int kCUs = 256;
+
+// Forward blocks resident on one CU, from the kernels' register use (at most
+// 512 VGPRs per SIMD lane: 128 a wave at four waves per SIMD, 256 at two) and
+// LDS: the d = dv = 64 kernel fits 128 registers, the wider ones do not.
+// Only the plan's schedule model uses it.
+constexpr int fwd_blocks_per_cu(int dtype, int d, int dv, int bq) {
+  return dtype != 0 ? 1 : (bq == kFwdBQ ? (d == 64 && dv == 64 ? 2 : 1)
+                                        : (d == 64 && dv == 64 ? 4 : 2));
+}
+
+// A forward item whose key range is cut into parts leaves, per part, the
+// unnormalised output rows and the running max and sum of its queries in a
+// partial-result slot; the last part to finish merges them.  Per wave and lane:
+// dv / 8 float4 of the output accumulator, then one float4 (max, sum, 0, 0),
+// stored chunk-major (chunk c of lane L at float4 64 c + L).
+constexpr int fwd_partial_chunks(int dv) { return dv / 8 + 1; }
+constexpr size_t fwd_partial_bytes(int dv, int bq) {
+  return (size_t)(bq / 32) * 64 * 16 * (size_t)fwd_partial_chunks(dv);
+}
 
 // One work item of the forward or dQ pass: attention head `head`, query slots
 // [q0, q1) inside one sequence, key slots [k0, k1) that any of those queries
 // may see.  For the dK/dV pass the roles swap: keys [q0, q1) of the item,
-// queries [k0, k1) that may see them.
+// queries [k0, k1) that may see them.  Backward lists: pad0 = stream, the
+// (attention head, sequence) index.  Forward list: pad0 = split group (-1:
+// the item is whole), pad1 = its partial-result slot, pad2 = part << 16 |
+// parts; the parts of a group hold consecutive slots.
 struct WorkItem {
   int32_t head;
   int32_t q0, q1;
@@ -84,11 +108,15 @@ struct attn_plan {
   std::vector<attn::WorkItem> fwd;  // forward items
   std::vector<attn::WorkItem> bwd;  // dK/dV items
   std::vector<attn::WorkItem> dq;   // dQ items (bf16 problems only)
+  int32_t fwd_groups = 0;           // forward items cut into parts
+  int32_t fwd_part_slots = 0;       // partial-result slots of their parts
+  std::vector<int32_t> zero_counters;  // initial merge counters (zeros)
   attn_plan_info info{};
 
   // Workspace layout (byte offsets; every section 256-byte aligned).
   size_t off_pos = 0, off_cos = 0, off_sin = 0, off_fwd = 0, off_bwd = 0, off_dq = 0;
   size_t off_delta = 0;
+  size_t off_split_cnt = 0, off_split_part = 0;
   size_t ws_bytes = 0;
   // Bound workspace.
   char *ws = nullptr;

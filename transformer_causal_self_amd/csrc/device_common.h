@@ -11,6 +11,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t uint32x4 __attribute__((ext_vector_type(4)));
 
 // bf16 halves of a 32-bit word -> float (exact widening).
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
@@ -61,6 +62,24 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// 16-byte stores and loads with the device-scope coherence bit (sc1 in the
+// cache-policy operand: bit 0 sc0, bit 1 nt, bit 4 sc1), the access form of
+// device-scope relaxed atomics: a store is visible to every CU of every XCD
+// once this wave's memory counter has drained (wait_stores), and a load reads
+// around the non-coherent cache levels.  They let blocks hand data to each
+// other through global memory without cache-wide write-backs or
+// invalidations.
+constexpr int kDeviceCoherent = 16;
+__device__ __forceinline__ void store16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                 floatx4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint32x4, v), r, off, 0,
+                                         kDeviceCoherent);
+}
+__device__ __forceinline__ floatx4 load16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0,
+                                                                           kDeviceCoherent));
+}
+
 // Direct global -> LDS staging (buffer_load_dwordx4 with the LDS flag) of
 // the 64 rows [t0, t0 + 64) of a [slots, heads, W] bf16 tensor into a
 // row-major LDS tile of row stride W + 8 elements.  A wave instruction writes
@@ -83,6 +102,8 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, __bf16 *lds, uin
 }
 // wait for this wave's staging loads (vmcnt 0; other counters left alone)
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// wait until this wave's stores are complete (vmcnt counts them too)
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // 2^x on the transcendental unit (v_exp_f32); results below the normal range
 // flush to zero, which is what softmax weights want.

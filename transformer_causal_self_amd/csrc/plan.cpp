@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstring>
 #include <new>
+#include <queue>
 
 #include <hip/hip_runtime_api.h>
 
@@ -58,33 +59,84 @@ void cut_items(std::vector<WorkItem> &out, int head, int stream, int64_t b, int6
 
 int64_t steps_of(const WorkItem &w, int step) { return (w.k1 - w.k0 + step - 1) / step; }
 
-// Order the work list for the 8 XCDs of the chip.  Workgroup i runs on XCD
-// i mod 8, and each XCD has its own L2, so items that read the same keys (one
-// head of one sequence, nearby tiles) should share an XCD.  Items arrive in
-// (head, sequence, tile) order; runs of `chunk` consecutive tiles of one head
-// and sequence form a chunk.  Chunks go to XCDs by longest-processing-time
-// (largest chunk to the least loaded XCD); inside an XCD, chunks and the items
-// of a chunk run longest first (causal load balance); position 8j + x of the
-// final list is the j-th item of XCD x.  (pad0 carries the stream index.)
-void order_for_xcds(std::vector<WorkItem> &v, int step, int chunk) {
+// A work item with its scheduling bookkeeping.  `stream` numbers the
+// (attention head, sequence) pairs; a query tile whose key range was cut into
+// `parts` pieces keeps its index `item` on every piece.
+struct Piece {
+  WorkItem w;
+  int64_t steps = 0;
+  int32_t stream = 0, item = 0, part = 0, parts = 1;
+};
+
+// The items as pieces; items of more than `limit` steps (of `step` partner
+// slots) are cut along their partner range at step boundaries:
+// mode 0 into ceil(n / limit) parts of (nearly) equal length, mode 1 into
+// parts of `limit` steps and a shorter last one.  Order is kept, the parts of
+// an item adjacent.
+std::vector<Piece> split_items(const std::vector<WorkItem> &v, int step, int64_t limit,
+                               int mode) {
+  std::vector<Piece> out;
+  out.reserve(v.size());
+  for (size_t i = 0; i < v.size(); ++i) {
+    const int64_t n = steps_of(v[i], step);
+    std::vector<int64_t> len;
+    if (n <= limit) {
+      len.push_back(n);
+    } else if (mode == 0) {
+      const int64_t parts = (n + limit - 1) / limit;
+      for (int64_t p = 0; p < parts; ++p) len.push_back(n / parts + (p < n % parts ? 1 : 0));
+    } else {
+      for (int64_t r = n; r > 0; r -= limit) len.push_back(std::min(r, limit));
+    }
+    int64_t at = 0;
+    for (size_t p = 0; p < len.size(); ++p) {
+      Piece c;
+      c.w = v[i];
+      c.w.k0 = (int32_t)std::min<int64_t>(v[i].k1, v[i].k0 + at * step);
+      c.w.k1 = (int32_t)std::min<int64_t>(v[i].k1, v[i].k0 + (at + len[p]) * step);
+      at += len[p];
+      c.steps = len[p];
+      c.stream = v[i].pad0;
+      c.item = (int32_t)i;
+      c.part = (int32_t)p;
+      c.parts = (int32_t)len.size();
+      out.push_back(c);
+    }
+  }
+  return out;
+}
+
+// Order pieces for the 8 XCDs of the chip.  Workgroup i runs on XCD i mod 8,
+// and each XCD has its own L2, so items that read the same keys (one head of
+// one sequence, nearby tiles) should share an XCD.  Pieces arrive in
+// (stream, tile) order; runs of `chunk` consecutive items of one stream form
+// a chunk (the parts of an item stay in its chunk).  Chunks go to XCDs by
+// longest-processing-time (largest chunk to the least loaded XCD).  Inside an
+// XCD the pieces run longest first (lpt = true), or chunk by chunk (the chunk
+// with the longest piece first, its pieces longest first; lpt = false), which
+// keeps fewer chunks' keys in flight at once.  Position 8j + x of the result
+// is the j-th piece of XCD x; an XCD that runs out takes the next piece of
+// the one with the most work left.
+std::vector<Piece> order_for_xcds(const std::vector<Piece> &v, int chunk, bool lpt) {
   constexpr int kXcd = 8;
   struct Chunk {
-    std::vector<WorkItem> items;
+    std::vector<Piece> pieces;
     int64_t work = 0, longest = 0;
+    int items = 0;
   };
   std::vector<Chunk> chunks;
   for (size_t i = 0; i < v.size(); ++i) {
-    const bool same_run = i > 0 && v[i].pad0 == v[i - 1].pad0;
-    if (!same_run || (int)chunks.back().items.size() == chunk) chunks.emplace_back();
+    const bool same_item = i > 0 && v[i].item == v[i - 1].item;
+    const bool same_run = i > 0 && v[i].stream == v[i - 1].stream;
+    if (!same_item && (!same_run || chunks.back().items == chunk)) chunks.emplace_back();
     Chunk &c = chunks.back();
-    c.items.push_back(v[i]);
-    c.work += steps_of(v[i], step);
-    c.longest = std::max<int64_t>(c.longest, steps_of(v[i], step));
+    if (!same_item) ++c.items;
+    c.pieces.push_back(v[i]);
+    c.work += v[i].steps;
+    c.longest = std::max<int64_t>(c.longest, v[i].steps);
   }
-  for (Chunk &c : chunks)
-    std::stable_sort(c.items.begin(), c.items.end(), [step](const WorkItem &a, const WorkItem &b) {
-      return steps_of(a, step) > steps_of(b, step);
-    });
+  const auto longer = [](const Piece &a, const Piece &b) { return a.steps > b.steps; };
+  for (Chunk &c : chunks) std::stable_sort(c.pieces.begin(), c.pieces.end(), longer);
   std::vector<size_t> order(chunks.size());
   for (size_t i = 0; i < order.size(); ++i) order[i] = i;
   std::stable_sort(order.begin(), order.end(),
@@ -96,30 +148,115 @@ void order_for_xcds(std::vector<WorkItem> &v, int step, int chunk) {
     load[x] += chunks[ci].work;
     xcd_chunks[x].push_back(ci);
   }
-  std::vector<std::vector<WorkItem>> q(kXcd);
+  std::vector<std::vector<Piece>> q(kXcd);
   for (int x = 0; x < kXcd; ++x) {
     std::stable_sort(xcd_chunks[x].begin(), xcd_chunks[x].end(),
                      [&](size_t a, size_t b) { return chunks[a].longest > chunks[b].longest; });
     for (size_t ci : xcd_chunks[x])
-      q[x].insert(q[x].end(), chunks[ci].items.begin(), chunks[ci].items.end());
+      q[x].insert(q[x].end(), chunks[ci].pieces.begin(), chunks[ci].pieces.end());
+    if (lpt) std::stable_sort(q[x].begin(), q[x].end(), longer);
   }
-  // interleave; an XCD that runs out is refilled from the one with most work left
   std::vector<size_t> head(kXcd, 0);
   std::vector<int64_t> left(kXcd, 0);
   for (int x = 0; x < kXcd; ++x)
-    for (const WorkItem &w : q[x]) left[x] += steps_of(w, step);
-  std::vector<WorkItem> out;
+    for (const Piece &c : q[x]) left[x] += c.steps;
+  std::vector<Piece> out;
   out.reserve(v.size());
   while (out.size() < v.size()) {
     const int x = (int)(out.size() % kXcd);
     int src = x;
     if (head[src] == q[src].size())
       src = (int)(std::max_element(left.begin(), left.end()) - left.begin());
-    const WorkItem w = q[src][head[src]++];
-    left[src] -= steps_of(w, step);
+    const Piece &c = q[src][head[src]++];
+    left[src] -= c.steps;
+    out.push_back(c);
+  }
+  return out;
+}
+
+// Makespan, in steps, of a launch order under a simple model of the chip:
+// workgroup i goes to XCD i mod 8, each XCD starts its workgroups in order on
+// `slots` block slots as they free up, and a block costs its steps plus one
+// (loading its queries, writing its rows), plus two more when it is one part
+// of a cut item (writing and reading the partial result).
+double simulated_makespan(const std::vector<Piece> &order, int slots) {
+  constexpr int kXcd = 8;
+  double makespan = 0.0;
+  for (int x = 0; x < kXcd; ++x) {
+    std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+    for (int s = 0; s < slots; ++s) free_at.push(0.0);
+    for (size_t i = x; i < order.size(); i += kXcd) {
+      const double t = free_at.top() + (double)order[i].steps + 1.0 + (order[i].parts > 1 ? 2.0 : 0.0);
+      free_at.pop();
+      free_at.push(t);
+      makespan = std::max(makespan, t);
+    }
+  }
+  return makespan;
+}
+
+// The forward work list as launched: the items cut (or not) so that the
+// simulated makespan is smallest over a few cut lengths around the mean load
+// of a block slot, and ordered for the XCDs.  A cut has to beat the uncut
+// list by 3%, which covers what the model leaves out (the merge traffic).
+// Returns the pieces; *groups receives the number of cut items.
+std::vector<WorkItem> schedule_forward(const std::vector<WorkItem> &items, int step, int chunk,
+                                       int slots_per_xcd, bool allow_split, int32_t *groups,
+                                       int32_t *part_slots) {
+  std::vector<Piece> best = order_for_xcds(split_items(items, step, INT64_MAX, 0), chunk, true);
+  double best_t = simulated_makespan(best, slots_per_xcd);
+  if (allow_split && !items.empty()) {
+    int64_t total = 0;
+    for (const WorkItem &w : items) total += steps_of(w, step);
+    const double mean = (double)total / (8.0 * slots_per_xcd);
+    const double uncut = best_t;
+    for (int mode = 0; mode < 2; ++mode)
+      for (int ai = 0; ai <= 20; ++ai) {  // cut lengths 0.3 .. 1.3 x the mean load
+        const int64_t limit = std::max<int64_t>(2, (int64_t)((0.3 + 0.05 * ai) * mean));
+        std::vector<Piece> c = order_for_xcds(split_items(items, step, limit, mode), chunk, true);
+        const double t = simulated_makespan(c, slots_per_xcd);
+        if (t < 0.97 * uncut && t < best_t) {
+          best_t = t;
+          best.swap(c);
+        }
+      }
+  }
+  // cut items: group index (counter) and partial-result slots, numbered in
+  // item order so the parts of one item have consecutive slots
+  std::vector<int32_t> parts_of(items.size(), 1), group_of(items.size(), -1),
+      first_slot(items.size(), -1);
+  for (const Piece &c : best) parts_of[(size_t)c.item] = c.parts;
+  int32_t ng = 0, ns = 0;
+  for (size_t i = 0; i < items.size(); ++i)
+    if (parts_of[i] > 1) {
+      group_of[i] = ng++;
+      first_slot[i] = ns;
+      ns += parts_of[i];
+    }
+  std::vector<WorkItem> out;
+  out.reserve(best.size());
+  for (const Piece &c : best) {
+    WorkItem w = c.w;
+    if (c.parts > 1) {
+      w.pad0 = group_of[(size_t)c.item];
+      w.pad1 = first_slot[(size_t)c.item] + c.part;
+      w.pad2 = (c.part << 16) | c.parts;
+    } else {
+      w.pad0 = -1;
+      w.pad1 = 0;
+      w.pad2 = 1;
+    }
     out.push_back(w);
   }
-  v.swap(out);
+  *groups = ng;
+  *part_slots = ns;
+  return out;
+}
+
+// The backward lists, uncut, chunk by chunk inside each XCD.
+void order_uncut(std::vector<WorkItem> &v, int step, int chunk) {
+  std::vector<Piece> o = order_for_xcds(split_items(v, step, INT64_MAX, 0), chunk, false);
+  for (size_t i = 0; i < v.size(); ++i) v[i] = o[i].w;
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -195,7 +332,9 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
     P.dv = dv;
     P.dtype = pr->dtype;
     P.causal = pr->causal;
-    P.window = pr->window > 0 ? pr->window : 0;
+    // A window that spans the longest sequence hides nothing: it is no
+    // window, which also keeps the kernels' slot + window sums inside int32.
+    P.window = pr->window > 0 && (int64_t)pr->window < max_len * mult ? pr->window : 0;
     P.scale = pr->softmax_scale == 0.0f ? (float)(1.0 / std::sqrt((double)pr->head_dim))
                                          : pr->softmax_scale;
     P.rope = pr->rope;
@@ -282,9 +421,13 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
         interleave(tb, p->bwd);  // per query head; grouped heads add into dK/dV
         ++stream;
       }
-    order_for_xcds(p->fwd, attn::kFwdBK, attn::kXcdChunk);
-    order_for_xcds(p->bwd, attn::kBwdBQ, attn::kXcdChunk);
-    order_for_xcds(p->dq, attn::kFwdBK, attn::kXcdChunk);
+    // forward: long query tiles are cut along their keys when that shortens
+    // the launch (bf16 kernels merge the parts); the backward lists stay whole
+    const int fwd_slots = attn::kCUs / 8 * attn::fwd_blocks_per_cu(P.dtype, P.d, P.dv, p->fwd_bq);
+    p->fwd = schedule_forward(p->fwd, attn::kFwdBK, attn::kXcdChunk, fwd_slots, bf16,
+                              &p->fwd_groups, &p->fwd_part_slots);
+    order_uncut(p->bwd, attn::kBwdBQ, attn::kXcdChunk);
+    order_uncut(p->dq, attn::kFwdBK, attn::kXcdChunk);
 
     const double elems = (double)P.N * P.H * P.d;       // Q, dQ
     const double kv_elems = (double)P.N * P.Hkv * P.d;  // K, dK
@@ -301,6 +444,7 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
     I.bwd_bytes = (elems + kv_elems + v_elems + 2.0 * o_elems) * es + lse_bytes +
                   (elems + kv_elems + v_elems) * 4.0;
     I.fwd_items = (int64_t)p->fwd.size();
+    I.fwd_split_items = p->fwd_groups;
     I.bwd_items = (int64_t)p->bwd.size();
     I.slots = P.Ns;
     I.attn_heads = P.Hs;
@@ -324,6 +468,11 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
     off = align256(off + sizeof(WorkItem) * p->dq.size());
     p->off_delta = off;
     off = align256(off + sizeof(float) * (size_t)P.Ns * P.Hs);
+    p->zero_counters.assign((size_t)p->fwd_groups, 0);
+    p->off_split_cnt = off;
+    off = align256(off + sizeof(int32_t) * (size_t)p->fwd_groups);
+    p->off_split_part = off;
+    off = align256(off + attn::fwd_partial_bytes(P.dv, p->fwd_bq) * (size_t)p->fwd_part_slots);
     p->ws_bytes = std::max<size_t>(off, 256);
   } catch (const std::bad_alloc &) {
     delete p;
@@ -352,6 +501,7 @@ attn_status attn_plan_bind(attn_plan *p, void *ws, size_t bytes, void *stream) {
       {p->off_fwd, p->fwd.data(), sizeof(WorkItem) * p->fwd.size()},
       {p->off_bwd, p->bwd.data(), sizeof(WorkItem) * p->bwd.size()},
       {p->off_dq, p->dq.data(), sizeof(WorkItem) * p->dq.size()},
+      {p->off_split_cnt, p->zero_counters.data(), sizeof(int32_t) * p->zero_counters.size()},
   };
   for (const Sec &s : secs) {
     if (s.n == 0) continue;
