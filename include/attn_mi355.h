@@ -300,6 +300,24 @@ attn_status attn_bwd(const attn_plan *plan, const void *q, const void *k, const 
                      float *dv, void *stream);
 
 /*
+ * attn_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation, arguments, results (bit for bit) and errors as
+ * attn_bwd, but its scratch (the D value of every attention head and slot,
+ * H' x N' floats) lives in a device array of the library of 32 MiB per GPU
+ * (kept until the process ends) instead of the plan's workspace.  The call
+ * itself allocates nothing.  Problems with H' x N' x 4 bytes above 32 MiB
+ * return ATTN_E_WORKSPACE.  Every call on one GPU shares that array (its
+ * contents are rewritten by each call before use), so calls that overlap on
+ * one GPU race: serialise them on one stream.  The stream's device (the
+ * current device for the null stream) is where the array is looked up, once
+ * per device, on its first call there.
+ */
+attn_status attn_bwd_noalloc(const attn_plan *plan, const void *q, const void *k, const void *v,
+                             const void *o, const float *lse, const void *d_o, float *dq,
+                             float *dk, float *dv, void *stream);
+
+/*
  * Backward of rope_qkv: the gradients with respect to its inputs q, k (before
  * the norm and the rotation), given the gradients d_q, d_k of its outputs
  * Q', K' as attn_bwd writes them.  Per head row: rotation by -phi at the same

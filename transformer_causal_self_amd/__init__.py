@@ -91,12 +91,14 @@ def load_library():
                                  vp, vp, vp, vp]
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.attn_bwd_noalloc.argtypes = lib.attn_bwd.argtypes
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_plan_destroy.argtypes = [vp]
     lib.attn_plan_destroy.restype = None
     for f in ("attn_plan_create", "attn_plan_bind", "attn_plan_stats", "attn_plan_work_items",
-              "rope_qkv", "rope_qkv_bwd", "rope_qkv_fp8", "attn_fwd", "attn_bwd"):
+              "rope_qkv", "rope_qkv_bwd", "rope_qkv_fp8", "attn_fwd", "attn_bwd",
+              "attn_bwd_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -319,9 +321,11 @@ def attn_fwd(plan: Plan, q, k, v, o=None, lse=None):
     return o, lse
 
 
-def attn_bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None):
+def attn_bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None, noalloc=False):
     """dQ float32 [N, H, d]; dK float32 [N, Hkv, d], dV float32 [N, Hkv, dv] (gradients
-    with respect to the rotated q, k and v)."""
+    with respect to the rotated q, k and v).  noalloc=True calls attn_bwd_noalloc (its
+    scratch in the library's device array instead of the plan's workspace); pass
+    dq, dk, dv to keep the call itself free of allocations."""
     for name, x, kv, vd in (("q", q, False, False), ("k", k, True, False), ("v", v, True, True),
                             ("o", o, False, True), ("do", do, False, True)):
         _need(plan, x, name, kv=kv, vd=vd)
@@ -332,7 +336,8 @@ def attn_bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None):
     for name, x, kv, vd in (("dq", dq, False, False), ("dk", dk, True, False),
                             ("dv", dv, True, True)):
         _need(plan, x, name, torch.float32, kv=kv, vd=vd)
-    _check("attn_bwd", load_library().attn_bwd(plan.handle, q.data_ptr(), k.data_ptr(),
+    name = "attn_bwd_noalloc" if noalloc else "attn_bwd"
+    _check(name, getattr(load_library(), name)(plan.handle, q.data_ptr(), k.data_ptr(),
                                                v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                                do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                                dv.data_ptr(), _stream(q.device)))

@@ -30,6 +30,8 @@
 //   (buffer loads with the LDS flag), double buffered: the next tile's loads
 //   are issued before the current tile's MMAs and waited for after them, and
 //   no staging register or LDS store instruction is spent on them.
+#include <mutex>
+
 #include "attn_internal.h"
 #include "device_common.h"
 #include "launch.h"
@@ -541,11 +543,10 @@ __global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ a, int64_
 template <int D, int DV = D>
 hipError_t launch_typed(const attn_plan *p, const void *q, const void *k, const void *v,
                         const void *o, const float *lse, const void *d_o, float *dq, float *dk,
-                        float *dv, hipStream_t stream) {
+                        float *dv, float *delta, hipStream_t stream) {
   const int Hs = p->p.Hs;
   const int64_t Ns = p->p.Ns;
   const float scale = p->p.scale, scale_log2 = p->p.scale * kLog2e;
-  float *delta = reinterpret_cast<float *>(p->ws + p->off_delta);
   const __bf16 *Q = static_cast<const __bf16 *>(q), *K = static_cast<const __bf16 *>(k);
   const __bf16 *V = static_cast<const __bf16 *>(v), *O = static_cast<const __bf16 *>(o);
   const __bf16 *G = static_cast<const __bf16 *>(d_o);
@@ -574,14 +575,71 @@ hipError_t launch_typed(const attn_plan *p, const void *q, const void *k, const 
 
 attn_status launch_bwd(const attn_plan *p, const void *q, const void *k, const void *v,
                        const void *o, const float *lse, const void *d_o, float *dq, float *dk,
-                       float *dv, hipStream_t stream) {
+                       float *dv, float *delta, hipStream_t stream) {
   const int d = p->p.d, w = p->p.dv;
   hipError_t e;
-  if (d == 64 && w == 64) e = launch_typed<64>(p, q, k, v, o, lse, d_o, dq, dk, dv, stream);
-  else if (d == 64) e = launch_typed<64, 128>(p, q, k, v, o, lse, d_o, dq, dk, dv, stream);
-  else if (w == 64) e = launch_typed<128, 64>(p, q, k, v, o, lse, d_o, dq, dk, dv, stream);
-  else e = launch_typed<128>(p, q, k, v, o, lse, d_o, dq, dk, dv, stream);
+  if (d == 64 && w == 64) e = launch_typed<64>(p, q, k, v, o, lse, d_o, dq, dk, dv, delta, stream);
+  else if (d == 64) e = launch_typed<64, 128>(p, q, k, v, o, lse, d_o, dq, dk, dv, delta, stream);
+  else if (w == 64) e = launch_typed<128, 64>(p, q, k, v, o, lse, d_o, dq, dk, dv, delta, stream);
+  else e = launch_typed<128>(p, q, k, v, o, lse, d_o, dq, dk, dv, delta, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
 }  // namespace attn
+
+// ------------------------------------------------------- allocation-free --
+// The backward's only scratch is D (one float per attention head and slot).
+// attn_bwd_noalloc keeps it in this array instead of the plan's workspace,
+// for callers that cannot allocate.  Each GPU the library runs on holds its
+// own copy until the process ends; host code uses the address that
+// hipGetSymbolAddress returns for the current device, never the name itself
+// (a host-side stand-in).
+static __device__ __align__(256) float scratch[attn::kNoallocScratchBytes / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch[kMaxDevices] = {};  // device address of `scratch`, per device
+
+// The address of `scratch` on the device that `stream` runs on (the current
+// device for the null stream), looked up once per device with that device
+// current.
+hipError_t scratch_on(hipStream_t stream, float **out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream != nullptr && (e = hipStreamGetDevice(stream, &dev)) != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = static_cast<float *>(ptr);
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" attn_status attn_bwd_noalloc(const attn_plan *p, const void *q, const void *k,
+                                        const void *v, const void *o, const float *lse,
+                                        const void *d_o, float *dq, float *dk, float *dv,
+                                        void *stream) {
+  const attn_status st = attn::check_bwd_args(p, q, k, v, o, lse, d_o, dq, dk, dv);
+  if (st != ATTN_OK || p->p.N == 0) return st;
+  if ((size_t)p->p.Hs * (size_t)p->p.Ns * sizeof(float) > attn::kNoallocScratchBytes)
+    return ATTN_E_WORKSPACE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  float *delta = nullptr;
+  if (scratch_on(hs, &delta) != hipSuccess) return ATTN_E_HIP;
+  return attn::launch_bwd(p, q, k, v, o, lse, d_o, dq, dk, dv, delta, hs);
+}

@@ -39,6 +39,10 @@ constexpr int kRopeThreads = 256;
 constexpr int kRopeFine = 64;
 // Work-list chunk: consecutive tiles of one head and sequence kept on one XCD.
 constexpr int kXcdChunk = 16;
+// Size of the device array that holds the backward's D values in
+// attn_bwd_noalloc (one float per attention head and slot: 8 Mi rows).
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+
 // Compute units of the chip (8 XCDs of 32).
 constexpr int kCUs = 256;
 

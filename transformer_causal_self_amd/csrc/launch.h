@@ -23,8 +23,15 @@ attn_status launch_rope_bwd(const attn_plan *p, const void *q, int64_t qs, const
 attn_status launch_fwd(const attn_plan *p, const void *q, const void *k, const void *v, void *o,
                        float *lse, hipStream_t stream);
 
+// delta: device scratch of Hs x Ns floats (D of every attention head and slot)
 attn_status launch_bwd(const attn_plan *p, const void *q, const void *k, const void *v,
                        const void *o, const float *lse, const void *d_o, float *dq, float *dk,
-                       float *dv, hipStream_t stream);
+                       float *dv, float *delta, hipStream_t stream);
+
+// The argument checks of attn_bwd (plan, dtype, binding, pointers, alignment);
+// ATTN_OK also for an empty problem, where nothing is launched.
+attn_status check_bwd_args(const attn_plan *p, const void *q, const void *k, const void *v,
+                           const void *o, const float *lse, const void *d_o, float *dq,
+                           float *dk, float *dv);
 
 }  // namespace attn

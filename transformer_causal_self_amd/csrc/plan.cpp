@@ -263,6 +263,24 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 }  // namespace
 
+namespace attn {
+
+attn_status check_bwd_args(const attn_plan *p, const void *q, const void *k, const void *v,
+                           const void *o, const float *lse, const void *d_o, float *dq,
+                           float *dk, float *dv) {
+  if (!p) return ATTN_E_INVALID;
+  if (p->p.dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
+  if (!p->ws) return ATTN_E_WORKSPACE;
+  if (p->p.N == 0) return ATTN_OK;
+  if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv) return ATTN_E_INVALID;
+  const void *ptrs[] = {q, k, v, o, lse, d_o, dq, dk, dv};
+  for (const void *x : ptrs)
+    if (!aligned16(x)) return ATTN_E_ALIGN;
+  return ATTN_OK;
+}
+
+}  // namespace attn
+
 extern "C" {
 
 const char *attn_status_str(attn_status s) {
@@ -622,15 +640,11 @@ attn_status attn_fwd(const attn_plan *p, const void *q, const void *k, const voi
 attn_status attn_bwd(const attn_plan *p, const void *q, const void *k, const void *v,
                      const void *o, const float *lse, const void *d_o, float *dq, float *dk,
                      float *dv, void *stream) {
-  if (!p) return ATTN_E_INVALID;
-  if (p->p.dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
-  if (!p->ws) return ATTN_E_WORKSPACE;
-  if (p->p.N == 0) return ATTN_OK;
-  if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv) return ATTN_E_INVALID;
-  const void *ptrs[] = {q, k, v, o, lse, d_o, dq, dk, dv};
-  for (const void *x : ptrs)
-    if (!aligned16(x)) return ATTN_E_ALIGN;
-  return attn::launch_bwd(p, q, k, v, o, lse, d_o, dq, dk, dv, static_cast<hipStream_t>(stream));
+  const attn_status st = attn::check_bwd_args(p, q, k, v, o, lse, d_o, dq, dk, dv);
+  if (st != ATTN_OK || p->p.N == 0) return st;
+  return attn::launch_bwd(p, q, k, v, o, lse, d_o, dq, dk, dv,
+                          reinterpret_cast<float *>(p->ws + p->off_delta),
+                          static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
