@@ -236,11 +236,42 @@ def test_fwd_edge_cases(case):
     assert_close(lse.cpu().double().numpy(), lse_ref, LSE_TOL, "LSE")
 
 
-@pytest.mark.parametrize("num", [4, 5])
-def test_fwd_deterministic(num):
+# problems whose plans cut long query tiles along their keys into parts that
+# separate blocks run and the last of them merges (d = 64 and 128, GQA, a
+# window longer than the cut, a separate value width)
+CUT = [
+    ("causal T=4000 H=2 d64", dataclasses.replace(W[5], n_tokens=4000, heads=2)),
+    ("causal T=2500 H=2 d128", dataclasses.replace(W[5], n_tokens=2500, heads=2, head_dim=128,
+                                                   rope=2)),
+    ("GQA T=3000 H=4 Hkv=1", dataclasses.replace(W[5], n_tokens=3000, heads=4, kv_heads=1)),
+    ("window 2500 T=4000", dataclasses.replace(W[5], n_tokens=4000, heads=2, window=2500)),
+    ("dv 128 T=3000", dataclasses.replace(W[5], n_tokens=3000, heads=2, v_dim=128)),
+]
+
+
+@pytest.mark.parametrize("case", CUT, ids=[c[0] for c in CUT])
+def test_fwd_cut_tiles(case):
+    name, w = case
+    w = dataclasses.replace(w, backward=False)
+    inp = wl.generate(w)
+    say(f"fwd with cut query tiles: {name}")
+    plan = make_plan(w, inp["cu"])
+    assert plan.info["fwd_split_items"] > 0
+    _, _, qt, kt = oracle_rotated(w, inp)
+    o, lse = run_fwd(w, plan, qt, kt, inp["v"])
+    if w.kv_heads:
+        o_ref, lse_ref = oracle.attn_fwd_gqa(f64(qt), f64(kt), f64(inp["v"]), inp["cu"], w.causal,
+                                             w.window, w.scale)
+    else:
+        o_ref, lse_ref = oracle_fwd(w, inp, qt, kt)
+    assert_close(o, o_ref, tol(w), "O", row_bound=5e-2)
+    assert_close(lse, lse_ref, LSE_TOL, "LSE")
+
+
+@pytest.mark.parametrize("w", [REDUCED[4], CUT[0][1]], ids=["varlen window", "cut tiles"])
+def test_fwd_deterministic(w):
     """Bit-identical results on a second launch, also where the plan cuts
     query tiles into parts that merge in whichever order they finish."""
-    w = REDUCED[num]
     inp = wl.generate(w)
     plan = make_plan(w, inp["cu"])
     q, k, v = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()

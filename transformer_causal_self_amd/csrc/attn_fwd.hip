@@ -261,9 +261,11 @@ __global__ __launch_bounds__(kFwdThreadsF32, fwd_min_blocks<T>()) void fwd_kerne
 // generic schedule above: K/V/Q come in through raw buffer loads whose
 // resource ends at the item's last key, so a ragged tail reads zeros without
 // branches and the per-tile address update is scalar; LDS is double-buffered
-// (one barrier per key tile); the running max is only moved when some lane's
-// tile max exceeds it by more than 2^8 in the exp2 domain (the weights stay
-// below 256, so nothing overflows, and O / l is unchanged).
+// (one barrier per key tile); the reference max of the exponentials is taken
+// on a wave's first tile and only moved when a lane's weights of a tile sum
+// past 2^64 (a score more than 64 above the reference in the exp2 domain), so
+// weights stay below 2^64 and sums of them far below the fp32 range, and
+// O / l and LSE do not depend on where the reference sits.
 
 // D: width of Q and K rows; DV: width of V and O rows.  K is kept row-major
 // (one key per row).  V has two layouts (VT):
