@@ -23,7 +23,9 @@ takes the most time; every kernel's own roofline is under `kernels`.
 `rows` (default run only) times rope_qkv and attn_fwd of the two varlen
 problems (65536 tokens, 6 heads, d = 128: paired window 128, and window 2048)
 with three input/output sets used in turn, so that each launch finds its data
-outside the 256 MiB last-level cache.  `copy_gbs` is a plain 1 GiB device
+outside the 256 MiB last-level cache: per launch (an event pair around each;
+`frac` is from their median) and back to back (one event pair around the
+run of launches, `*_back_to_back`, which pays the launch gap once).  `copy_gbs` is a plain 1 GiB device
 copy (read + write bytes over its time), the practical HBM ceiling.
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same
 workload on the host cores.
@@ -177,29 +179,46 @@ def varlen_rows(dev, reps=10, sets=3):
                              o=torch.empty_like(q),
                              lse=torch.empty((info["attn_heads"], info["slots"]),
                                              dtype=torch.float32, device=dev)))
+        def launch(name, b):
+            if name == "rope_qkv":
+                tca.rope_qkv(plan, b["q"], b["k"], q_out=b["q2"], k_out=b["k2"])
+            else:
+                tca.attn_fwd(plan, b["q2"], b["k2"], b["v"], b["o"], b["lse"])
+
         ev = {"rope_qkv": [], "attn_fwd": []}
         for r in range(2 + reps):
             b = bufs[r % sets]
-            for name, fn in (("rope_qkv", lambda: tca.rope_qkv(plan, b["q"], b["k"],
-                                                              q_out=b["q2"], k_out=b["k2"])),
-                             ("attn_fwd", lambda: tca.attn_fwd(plan, b["q2"], b["k2"], b["v"],
-                                                              b["o"], b["lse"]))):
+            for name in ev:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
-                fn()
+                launch(name, b)
                 e1.record()
                 if r >= 2:
                     ev[name].append((e0, e1))
+        # the same launches back to back, one event pair around the run: the
+        # launch gap that each single-launch event pair includes is paid once
+        batch = {}
+        for name in ev:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for r in range(reps):
+                launch(name, bufs[r % sets])
+            e1.record()
+            batch[name] = (e0, e1)
         torch.cuda.synchronize()
         row = {"workload": w.name, "sets": sets, "reps": reps}
         for name in ev:
             mean, med, mn = stats_ms(ev[name])
+            bt = batch[name][0].elapsed_time(batch[name][1]) / reps
             if name == "rope_qkv":
                 by = info["rope_bytes"]
                 row[name] = {"bound": "hbm", "gbs_median": by / (med * 1e-3) / 1e9,
                              "gbs_best": by / (mn * 1e-3) / 1e9,
                              "frac": by / (med * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                             "ms_mean": mean, "ms_median": med, "ms_min": mn}
+                             "gbs_back_to_back": by / (bt * 1e-3) / 1e9,
+                             "frac_back_to_back": by / (bt * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                             "ms_mean": mean, "ms_median": med, "ms_min": mn,
+                             "ms_back_to_back": bt}
             else:
                 fl, by = info["fwd_flops"], info["fwd_bytes"]
                 if fl / by >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
@@ -209,7 +228,7 @@ def varlen_rows(dev, reps=10, sets=3):
                     row[name] = {"bound": "hbm", "gbs_median": by / (med * 1e-3) / 1e9,
                                  "frac": by / (med * 1e-3) / 1e9 / PEAK_HBM_GBS,
                                  "tflops_median": fl / (med * 1e-3) / 1e12}
-                row[name].update(ms_mean=mean, ms_median=med, ms_min=mn)
+                row[name].update(ms_mean=mean, ms_median=med, ms_min=mn, ms_back_to_back=bt)
         out[f"problem{num}"] = row
         del bufs, base, plan
         torch.cuda.empty_cache()
