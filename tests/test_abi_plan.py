@@ -113,29 +113,29 @@ def test_empty_problem_is_valid():
 
 
 def test_item_sizes_follow_the_dtype():
-    # bf16: 256-query forward items, 128-row backward dK/dV (keys) and dQ
-    # (queries) items; fp32 (no backward): 128-query forward items and empty
-    # backward lists
+    # bf16: 256-query forward items at a head width of 128, 128-query ones at
+    # widths of 64, 128-row backward dK/dV (keys) and dQ (queries) items;
+    # fp32 (no backward): 128-query forward items and empty backward lists
     cu = [0, 2100]
     pb = plan(num_tokens=2100, cu_seqlens=cu)
     pb128 = plan(num_tokens=2100, cu_seqlens=cu, head_dim=128)
     pf = plan(num_tokens=2100, cu_seqlens=cu, dtype="fp32")
     rows = lambda p, which: np.diff(p.work_items(which)[:, 1:3], axis=1).max()
-    assert rows(pb, 0) == 256 and rows(pb, 1) == 128 and rows(pb, 2) == 128
+    assert rows(pb, 0) == 128 and rows(pb, 1) == 128 and rows(pb, 2) == 128
     assert rows(pb128, 0) == 256 and rows(pb128, 1) == 128 and rows(pb128, 2) == 128
     for d, dv in ((64, 128), (128, 64)):
         pm = plan(num_tokens=2100, cu_seqlens=cu, head_dim=d, v_head_dim=dv)
-        assert rows(pm, 1) == 128 and rows(pm, 2) == 128
+        assert rows(pm, 0) == 256 and rows(pm, 1) == 128 and rows(pm, 2) == 128
     assert rows(pf, 0) == 128
-    # a short window keeps 128-query forward items (a longer one does not)
-    assert np.diff(plan(num_tokens=2100, cu_seqlens=cu, window=512).work_items(0)[:, 1:3],
-                   axis=1).max() == 128
-    assert np.diff(plan(num_tokens=2100, cu_seqlens=cu, window=513).work_items(0)[:, 1:3],
-                   axis=1).max() == 256
+    # at width 128 a short window keeps 128-query forward items (a longer one
+    # does not)
+    wide = dict(num_tokens=2100, cu_seqlens=cu, head_dim=128)
+    assert rows(plan(window=512, **wide), 0) == 128
+    assert rows(plan(window=513, **wide), 0) == 256
     # so do problems whose sequences all have at most 2048 slots (paired: 1024 tokens)
-    assert rows(plan(num_tokens=2048, cu_seqlens=[0, 2048]), 0) == 128
-    assert rows(plan(num_tokens=2049, cu_seqlens=[0, 2049]), 0) == 256
-    assert rows(plan(num_tokens=1025, cu_seqlens=[0, 1025], paired=1), 0) == 256
+    assert rows(plan(num_tokens=2048, cu_seqlens=[0, 2048], head_dim=128), 0) == 128
+    assert rows(plan(num_tokens=2049, cu_seqlens=[0, 2049], head_dim=128), 0) == 256
+    assert rows(plan(num_tokens=1025, cu_seqlens=[0, 1025], paired=1, head_dim=128), 0) == 256
     assert len(pf.work_items(1)) == 0 and len(pf.work_items(2)) == 0
     for bad in (-1, 3):
         with pytest.raises(tca.AttnError):
@@ -214,7 +214,7 @@ def test_long_causal_forward_is_cut_and_balanced_one_is_not():
     assert p.info["fwd_split_items"] > 0
     assert p.info["fwd_split_items"] == len({int(g) for g in fwd[:, 5] if g >= 0})
     whole = whole_items(fwd)
-    assert len(whole) == 12 * 64
+    assert len(whole) == 12 * 16384 // 128  # 128-query tiles at head width 64
     steps = (fwd[:, 4] - fwd[:, 3] + 63) // 64
     assert steps.max() < 256
     # many tiles of similar length over the whole chip: nothing to gain

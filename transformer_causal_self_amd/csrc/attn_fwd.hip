@@ -12,8 +12,9 @@
 //
 // gfx950 mapping (one work item = one block of 8 waves = 256 query slots of
 // one attention head for bf16, 4 waves = 128 slots for fp32, for windows of
-// at most 512 slots and when every sequence fits 2048 slots; each wave owns
-// 32 query slots, and every K/V tile staged in LDS serves the whole block):
+// at most 512 slots, when every sequence fits 2048 slots and at head widths
+// of 64; each wave owns 32 query slots, and every K/V tile staged in LDS
+// serves the whole block):
 //   * Each wave holds its 32 queries as the B operand of
 //     v_mfma_f32_32x32x16_bf16 for the whole item (registers).
 //   * K tiles of 64 key slots are staged in LDS row-major.  V tiles are staged
@@ -277,9 +278,9 @@ __global__ __launch_bounds__(kFwdThreadsF32, fwd_min_blocks<T>()) void fwd_kerne
 //               two ds_read_b64_tr_b16, which run at half the rate of
 //               16-byte reads.
 // Eight-wave items read every staged tile eight times and use VT = true;
-// four-wave items (short windows, short sequences) use VT = false, where the
-// cheaper store wins (10% on the paired window-128 problem; the other way
-// round costs 3-7% on eight-wave items).
+// four-wave items (short windows, short sequences, head widths of 64) use
+// VT = false, where the cheaper store wins (10% on the paired window-128
+// problem; the other way round costs 3-7% on eight-wave items).
 template <int D, int DV, bool VT>
 struct SmemBF {
   static constexpr int KS = D + 8;                 // K row stride (elements): 4-bank shift

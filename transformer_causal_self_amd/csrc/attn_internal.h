@@ -15,9 +15,15 @@ namespace attn {
 //   forward: BQ query slots per work item, BK key slots per inner step, 32
 //   queries per wave.  bf16 runs eight waves per item (each staged K/V tile
 //   serves 256 queries) unless the window is short, where a 256-query item
-//   would stage mostly keys that most of its waves skip, or every sequence is
-//   short, where twice as many items balance the CUs better: then four.  fp32
-//   runs four, its registers do not allow more.
+//   would stage mostly keys that most of its waves skip, every sequence is
+//   short, where twice as many items balance the CUs better, or both head
+//   widths are 64: then four.  At widths of 64 four four-wave blocks share a
+//   CU (two eight-wave ones otherwise), their waves independent of each
+//   other on each SIMD, which beats staging each K/V tile once for 256
+//   queries (+2% on the long causal problem, +3% with grouped K/V heads);
+//   wider heads fit one eight-wave or two four-wave blocks per CU, and there
+//   the four-wave items lose 3% (varlen window-2048 problem).  fp32 runs
+//   four, its registers do not allow more.
 constexpr int kFwdBQ = 256;
 constexpr int kFwdBQShort = 128;
 constexpr int kFwdShortWindow = 512;  // windows up to this use kFwdBQShort

@@ -402,7 +402,7 @@ attn_status attn_plan_create(const attn_problem *pr, attn_plan **out) {
     int stream = 0;
     const bool bf16 = P.dtype == ATTN_BF16;  // the backward is bf16 only
     const bool short_rows = (P.window > 0 && P.window <= attn::kFwdShortWindow) ||
-                            max_len * mult <= attn::kFwdShortSeq;
+                            max_len * mult <= attn::kFwdShortSeq || (P.d == 64 && P.dv == 64);
     p->fwd_bq = !bf16 ? attn::kFwdBQF32 : short_rows ? attn::kFwdBQShort : attn::kFwdBQ;
     // One stream per (K/V head, sequence).  With grouped K/V heads, the items
     // of the group's query heads are interleaved tile by tile, so the ones
