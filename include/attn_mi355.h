@@ -189,8 +189,8 @@ attn_status attn_plan_stats(const attn_plan *plan, attn_plan_info *info);
 /*
  * Introspection of the tile work lists (host only), for testing and
  * scheduling analysis.  which = 0: forward items (256 query slots each for
- * bf16; 128 for fp32, for windows of at most 512 slots and when no sequence
- * is longer than 2048 slots); which = 1:
+ * bf16; 128 for fp32, for windows of at most 512 slots, when no sequence is
+ * longer than 2048 slots and at head widths d = dv = 64); which = 1:
  * backward key-tile items (128 key slots); which = 2: backward dQ items (128
  * query slots).  The backward lists are empty for fp32 problems.  The head
  * of every item is a query (attention) head; with grouped K/V heads the key
